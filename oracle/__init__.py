@@ -1,0 +1,19 @@
+"""CPU float64 oracle for block-paged KV attention.
+
+TEST INFRASTRUCTURE ONLY.  The test-suite, the smoke check and the
+benchmark's CPU-baseline leg may import this package; the library
+(``block_paged_kv_append_amd``) never does and shares no code with it.
+"""
+from .paged_attention import (  # noqa: F401
+    BLOCK,
+    append,
+    attend,
+    decode,
+    decode_splitk,
+    gather_sequence,
+    merge_partials,
+    prefill,
+    scores,
+    values,
+    visible,
+)

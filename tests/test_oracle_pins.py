@@ -1,0 +1,558 @@
+"""Pins for the CPU oracle: each test ties ``oracle`` to something other than
+itself -- a library routine (torch SDPA in float64), closed forms, invariants,
+brute force on tiny inputs -- so that a dropped term, a wrong sign or index, or
+a transposed operand anywhere in it fails at least one test.
+
+Pin map (the oracle function each one guards):
+  P1  gather + attend       vs a loop-nest textbook attention on contiguous K/V
+  P2  decode, prefill       vs torch SDPA (CPU, float64, explicit boolean mask)
+  P3  attend                softmax rows sum to 1, p >= 0, p == 0 off-mask
+  P4  gather                physical block placement does not change outputs
+  P5  visible               brute-force window / causal / length masks
+  P6  decode                closed forms (constant V, q = 0, equal keys, W = 1, L = 1)
+  P7  decode_splitk         equals decode for many partition sizes
+  P8  prefill               row j == decode at length L - n + j + 1
+  P9  gather                shared (refcounted) prefix == private copies
+  P10 append                round trip, untouched slots, skipped / bad slots
+  P11 scores                softcap limits
+  P12 decode                GQA == replicated single-head attention
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_paged_kv_append_amd import workloads as wl
+
+BS = 16
+
+
+# ---------------------------------------------------------------------------
+# test-local helpers, written independently of the oracle
+# ---------------------------------------------------------------------------
+def scatter_contiguous(K, V, dtype, num_blocks=None, table=None):
+    """Place contiguous per-kv-head rows ``K, V [Hkv, L, D]`` (float32 values)
+    into a fresh pool.  Token t of the sequence goes to block ``table[t // 16]``
+    (identity table by default), offset ``t % 16``; unused slots are NaN."""
+    Hkv, L, D = K.shape
+    X = 16 // (2 if dtype == "bf16" else 4)
+    nblk = (L + BS - 1) // BS
+    if table is None:
+        table = np.arange(nblk, dtype=np.int32)
+    NB = num_blocks or int(max(table[:nblk]) + 1 if nblk else 1)
+    kshape, vshape = wl.pool_shapes(NB, Hkv, D, dtype)
+    kp = np.full(kshape, wl.nan_bits(dtype))
+    vp = np.full(vshape, wl.nan_bits(dtype))
+    kb = wl.to_bits(K, dtype)
+    vb = wl.to_bits(V, dtype)
+    for g in range(Hkv):
+        for t in range(L):
+            blk, off = int(table[t // BS]), t % BS
+            for d in range(D):
+                kp[blk, g, d // X, off, d % X] = kb[g, t, d]
+                vp[blk, g, d, off] = vb[g, t, d]
+    return kp, vp, np.asarray(table, dtype=np.int32)
+
+
+def textbook(q, K, V, scale, softcap, keep):
+    """Two-pass softmax attention with Python loops and math.exp."""
+    n = len(K)
+    s = []
+    for t in range(n):
+        dot = 0.0
+        for d in range(len(q)):
+            dot += float(q[d]) * float(K[t][d])
+        x = scale * dot
+        if softcap > 0:
+            x = softcap * math.tanh(x / softcap)
+        s.append(x)
+    idx = [t for t in range(n) if keep(t)]
+    m = max(s[t] for t in idx)
+    e = {t: math.exp(s[t] - m) for t in idx}
+    z = sum(e.values())
+    out = [sum(e[t] * float(V[t][d]) for t in idx) / z for d in range(len(V[0]))]
+    return out, m + math.log(z)
+
+
+def f32vals(bits, dtype):
+    return wl.bits_to_f32(bits, dtype).astype(np.float64)
+
+
+def rand_f32(rng, shape, dtype):
+    """Random values already representable in ``dtype``."""
+    x = rng.standard_normal(shape).astype(np.float32)
+    return wl.bits_to_f32(wl.to_bits(x, dtype), dtype).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# P1 dense equivalence
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("softcap,window", [(0.0, 0), (2.0, 0), (0.0, 9), (3.0, 20)])
+def test_p1_paged_equals_loop_nest(dtype, softcap, window):
+    rng = np.random.default_rng(11)
+    Hkv, G, L, D = 2, 2, 37, 16
+    K = rand_f32(rng, (Hkv, L, D), dtype)
+    V = rand_f32(rng, (Hkv, L, D), dtype)
+    qv = rand_f32(rng, (1, Hkv * G, D), dtype)
+    kp, vp, table = scatter_contiguous(K, V, dtype)
+    bt = np.zeros((1, 4), dtype=np.int32)
+    bt[0, :3] = table
+    scale = 0.3
+    out, lse = oracle.decode(wl.to_bits(qv, dtype), kp, vp, bt, np.array([L]), scale, softcap,
+                             window, dtype)
+    for h in range(Hkv * G):
+        g = h // G
+        ref, ref_lse = textbook(qv[0, h], K[g], V[g], scale, softcap,
+                                lambda t: window <= 0 or (L - 1 - t) < window)
+        np.testing.assert_allclose(out[0, h], ref, rtol=0, atol=1e-12)
+        assert abs(lse[0, h] - ref_lse) <= 1e-12
+
+
+def test_p1_prefill_loop_nest():
+    rng = np.random.default_rng(12)
+    dtype, Hkv, G, L, n, D = "bf16", 1, 2, 29, 7, 16
+    K = rand_f32(rng, (Hkv, L, D), dtype)
+    V = rand_f32(rng, (Hkv, L, D), dtype)
+    qv = rand_f32(rng, (n, Hkv * G, D), dtype)
+    kp, vp, table = scatter_contiguous(K, V, dtype)
+    bt = table[None, :]
+    out, lse = oracle.prefill(wl.to_bits(qv, dtype), np.array([0, n]), kp, vp, bt, np.array([L]),
+                              0.25, 0.0, 0, dtype)
+    for j in range(n):
+        qp = L - n + j
+        for h in range(G):
+            ref, ref_lse = textbook(qv[j, h], K[0], V[0], 0.25, 0.0, lambda t: t <= qp)
+            np.testing.assert_allclose(out[j, h], ref, rtol=0, atol=1e-12)
+            assert abs(lse[j, h] - ref_lse) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# P2 library routine: torch SDPA on CPU in float64
+# ---------------------------------------------------------------------------
+def sdpa(q, K, V, keep, scale):
+    """q [Hq, n, D], K/V [Hq, L, D], keep [n, L] bool -> [Hq, n, D]."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float64))
+    o = torch.nn.functional.scaled_dot_product_attention(
+        t(q)[None], t(K)[None], t(V)[None], attn_mask=torch.from_numpy(keep)[None, None],
+        scale=scale)
+    return o[0].numpy()
+
+
+@pytest.mark.parametrize("window", [0, 5, 16, 33])
+def test_p2_decode_vs_torch_sdpa(window):
+    rng = np.random.default_rng(21)
+    dtype, Hkv, G, D = "bf16", 2, 4, 32
+    lens = [1, 16, 17, 45]
+    MB = 3
+    B = len(lens)
+    NB = B * MB
+    kshape, vshape = wl.pool_shapes(NB, Hkv, D, dtype)
+    kp = np.full(kshape, wl.nan_bits(dtype))
+    vp = np.full(vshape, wl.nan_bits(dtype))
+    bt = np.zeros((B, MB), dtype=np.int32)
+    qv = rand_f32(rng, (B, Hkv * G, D), dtype)
+    Ks, Vs = [], []
+    for b, L in enumerate(lens):
+        K = rand_f32(rng, (Hkv, L, D), dtype)
+        V = rand_f32(rng, (Hkv, L, D), dtype)
+        table = np.arange(b * MB, b * MB + MB, dtype=np.int32)[::-1].copy()
+        kb, vb, _ = scatter_contiguous(K, V, dtype, NB, table)
+        nblk = (L + BS - 1) // BS
+        for j in range(nblk):
+            kp[table[j]] = kb[table[j]]
+            vp[table[j]] = vb[table[j]]
+        bt[b] = table
+        Ks.append(K)
+        Vs.append(V)
+    scale = 1 / math.sqrt(D)
+    out, _ = oracle.decode(wl.to_bits(qv, dtype), kp, vp, bt, np.array(lens), scale, 0.0, window,
+                           dtype)
+    for b, L in enumerate(lens):
+        keep = np.array([[window <= 0 or (L - 1 - t) < window for t in range(L)]])
+        Krep = np.repeat(Ks[b], G, axis=0)
+        Vrep = np.repeat(Vs[b], G, axis=0)
+        ref = sdpa(qv[b][:, None, :], Krep, Vrep, keep, scale)[:, 0, :]
+        np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("window", [0, 7])
+def test_p2_prefill_vs_torch_sdpa(window):
+    rng = np.random.default_rng(22)
+    dtype, Hkv, G, D = "bf16", 2, 2, 16
+    L, n = 40, 13
+    K = rand_f32(rng, (Hkv, L, D), dtype)
+    V = rand_f32(rng, (Hkv, L, D), dtype)
+    qv = rand_f32(rng, (n, Hkv * G, D), dtype)
+    kp, vp, table = scatter_contiguous(K, V, dtype)
+    out, _ = oracle.prefill(wl.to_bits(qv, dtype), np.array([0, n]), kp, vp, table[None, :],
+                            np.array([L]), 0.5, 0.0, window, dtype)
+    keep = np.array([[t <= L - n + j and (window <= 0 or L - n + j - t < window)
+                      for t in range(L)] for j in range(n)])
+    ref = sdpa(qv.transpose(1, 0, 2), np.repeat(K, G, 0), np.repeat(V, G, 0), keep, 0.5)
+    np.testing.assert_allclose(out, ref.transpose(1, 0, 2), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P3 softmax normalisation, read through a one-hot V
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("window,softcap", [(0, 0.0), (11, 0.0), (0, 1.5)])
+def test_p3_probabilities_sum_to_one(window, softcap):
+    rng = np.random.default_rng(31)
+    dtype, L, D = "f32", 53, 64
+    K = rand_f32(rng, (1, L, D), dtype) * 2
+    V = np.zeros((1, L, D), dtype=np.float32)
+    V[0, np.arange(L), np.arange(L)] = 1.0  # V[t] = e_t: the output is the probability row
+    qv = rand_f32(rng, (1, 3, D), dtype)
+    kp, vp, table = scatter_contiguous(K, V, dtype)
+    out, _ = oracle.decode(wl.to_bits(qv, dtype), kp, vp, table[None, :], np.array([L]), 0.4,
+                           softcap, window, dtype)
+    vis = np.array([window <= 0 or (L - 1 - t) < window for t in range(L)])
+    for h in range(3):
+        p = out[0, h, :L]
+        assert abs(p.sum() - 1.0) <= 1e-12
+        assert (p >= 0).all()
+        assert (p[~vis] == 0).all()
+        assert (p[vis] > 0).all()
+        assert (out[0, h, L:] == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# P4 placement invariance
+# ---------------------------------------------------------------------------
+def test_p4_block_placement_invariance():
+    case = wl.make_decode_case(41, [5, 33, 64, 70], 4, 2, 32, "bf16", softcap=5.0, window=40)
+    args = (case.scale, case.softcap, case.window, case.dtype)
+    out0, lse0 = oracle.decode(case.q, case.k_pool, case.v_pool, case.block_tables,
+                               case.context_lens, *args)
+    perm = np.random.default_rng(42).permutation(case.num_blocks)
+    kp = np.empty_like(case.k_pool)
+    vp = np.empty_like(case.v_pool)
+    kp[perm] = case.k_pool
+    vp[perm] = case.v_pool
+    bt = perm[case.block_tables].astype(np.int32)
+    out1, lse1 = oracle.decode(case.q, kp, vp, bt, case.context_lens, *args)
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+# ---------------------------------------------------------------------------
+# P5 brute-force masks
+# ---------------------------------------------------------------------------
+def test_p5_visibility_brute_force():
+    for L in range(1, 41):
+        for W in sorted({1, 15, 16, 17, L, 0}):
+            for causal in (True, False):
+                for q_pos in range(L):
+                    got = oracle.visible(q_pos, L, W, causal)
+                    for t in range(L):
+                        want = True
+                        if causal and t > q_pos:
+                            want = False
+                        if W > 0 and not (q_pos - t < W):
+                            want = False
+                        assert bool(got[t]) == want, (L, W, causal, q_pos, t)
+                    if W > 0 and causal:
+                        assert got.sum() == min(W, q_pos + 1)
+
+
+def test_p5_decode_window_counts():
+    """With q = 0 all logits are 0, so lse = ln(number of visible keys)."""
+    for L in (1, 15, 16, 17, 40):
+        for W in (0, 1, 15, 16, 17, L):
+            case = wl.make_decode_case(51, [L], 2, 1, 16, "f32", window=W)
+            q = np.zeros_like(case.q)
+            _, lse = oracle.decode(q, case.k_pool, case.v_pool, case.block_tables,
+                                   case.context_lens, 1.0, 0.0, W, "f32")
+            n_vis = L if W <= 0 else min(W, L)
+            np.testing.assert_allclose(lse, math.log(n_vis), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P6 closed forms
+# ---------------------------------------------------------------------------
+def _contig_case(rng, L, D, dtype="f32", Hq=2):
+    K = rand_f32(rng, (1, L, D), dtype)
+    V = rand_f32(rng, (1, L, D), dtype)
+    q = rand_f32(rng, (1, Hq, D), dtype)
+    return K, V, q
+
+
+@pytest.mark.parametrize("window,softcap", [(0, 0.0), (6, 0.0), (0, 4.0)])
+def test_p6_closed_forms(window, softcap):
+    rng = np.random.default_rng(61)
+    L, D = 35, 8
+    K, V, q = _contig_case(rng, L, D)
+    vis = np.array([window <= 0 or (L - 1 - t) < window for t in range(L)])
+
+    def run(K, V, q, L=L, window=window):
+        kp, vp, table = scatter_contiguous(K, V, "f32")
+        return oracle.decode(wl.to_bits(q, "f32"), kp, vp, table[None, :], np.array([L]), 0.7,
+                             softcap, window, "f32")
+
+    # constant V -> output is that constant
+    Vc = np.full(V.shape, 0.375)
+    out, _ = run(K, Vc, q)
+    np.testing.assert_allclose(out, 0.375, rtol=0, atol=1e-12)
+    # q = 0 -> uniform weights -> mean of the visible V rows
+    out, _ = run(K, V, np.zeros_like(q))
+    np.testing.assert_allclose(out[0, 0], V[0, vis].mean(0), rtol=0, atol=1e-12)
+    # all keys equal -> uniform weights as well
+    Ke = np.repeat(K[:, :1], L, axis=1)
+    out, _ = run(Ke, V, q)
+    np.testing.assert_allclose(out[0, 1], V[0, vis].mean(0), rtol=0, atol=1e-12)
+    # window 1 -> only the query's own token
+    out, _ = run(K, V, q, window=1)
+    np.testing.assert_allclose(out[0, 0], V[0, L - 1], rtol=0, atol=1e-12)
+    # a single cached token
+    out, lse = run(K[:, :1], V[:, :1], q, L=1)
+    np.testing.assert_allclose(out[0, 1], V[0, 0], rtol=0, atol=1e-12)
+
+
+def test_p6_two_key_closed_form():
+    """q.k0 = 2, q.k1 = 0 at scale 0.5 -> logits (1, 0), weights
+    (e, 1)/(e + 1), lse = ln(1 + e); with softcap 1 the first logit is tanh(1)."""
+    D = 4
+    K = np.zeros((1, 2, D), np.float32)
+    K[0, 0, 0] = 2.0
+    V = np.zeros((1, 2, D), np.float32)
+    V[0, 0, 0] = 1.0
+    V[0, 1, 1] = 1.0
+    q = np.zeros((1, 1, D), np.float32)
+    q[0, 0, 0] = 1.0
+    kp, vp, table = scatter_contiguous(K, V, "f32")
+    for cap, s0 in ((0.0, 1.0), (1.0, math.tanh(1.0))):
+        out, lse = oracle.decode(wl.to_bits(q, "f32"), kp, vp, table[None, :], np.array([2]), 0.5,
+                                 cap, 0, "f32")
+        e = math.exp(s0)
+        np.testing.assert_allclose(out[0, 0], [e / (e + 1), 1 / (e + 1), 0, 0], rtol=0,
+                                   atol=1e-15)
+        assert abs(lse[0, 0] - math.log(1 + e)) <= 1e-15
+
+
+# ---------------------------------------------------------------------------
+# P7 split-K merge identity
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("P", [1, 16, 17, 48, 512, 1000])
+@pytest.mark.parametrize("window", [0, 20, 100])
+def test_p7_splitk_equals_decode(P, window):
+    case = wl.make_decode_case(71, [1, 20, 97, 300], 4, 2, 16, "bf16", softcap=3.0,
+                               window=window)
+    a = (case.q, case.k_pool, case.v_pool, case.block_tables, case.context_lens, case.scale,
+         case.softcap, case.window, case.dtype)
+    out, lse = oracle.decode(*a)
+    out_s, lse_s, parts = oracle.decode_splitk(*a, partition_size=P)
+    np.testing.assert_allclose(out_s, out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse_s, lse, rtol=0, atol=1e-12)
+    if window and P < 300 - window:
+        assert any(l == 0 for (_, l, _) in parts.values()), "some partition should be empty"
+
+
+def test_p7_merge_of_two_halves():
+    """Merging the partials of two disjoint key sets equals attending over their union."""
+    rng = np.random.default_rng(72)
+    K = rng.standard_normal((30, 8))
+    V = rng.standard_normal((30, 8))
+    q = rng.standard_normal((1, 8))
+    full, full_lse = oracle.attend(q, K, V, [29], 1.0, causal=False)
+    parts = []
+    for idx in (np.arange(0, 11), np.arange(11, 30)):
+        o, lse = oracle.attend(q, K[idx], V[idx], [100], 1.0, causal=False)
+        m = lse[0]  # (m, l) = (lse, 1) is an equivalent encoding of the same partial
+        parts.append((m, 1.0, o[0]))
+    parts.append((-np.inf, 0.0, np.zeros(8)))  # an empty partition contributes nothing
+    out, lse = oracle.merge_partials(parts)
+    np.testing.assert_allclose(out, full[0], rtol=0, atol=1e-12)
+    assert abs(lse - full_lse[0]) <= 1e-12
+
+
+# ---------------------------------------------------------------------------
+# P8 prefill / decode consistency
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("window", [0, 10])
+def test_p8_prefill_rows_are_decodes(window):
+    case = wl.make_prefill_case(81, [20, 33], [13, 5], 4, 2, 16, "bf16", window=window,
+                                softcap=2.0)
+    kp, vp = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           case.dtype)
+    out, lse = oracle.prefill(case.q, case.cu_q_lens, kp, vp, case.block_tables,
+                              case.context_lens, case.scale, case.softcap, window, case.dtype)
+    for b in range(case.num_seqs):
+        n, L = int(case.q_lens[b]), int(case.context_lens[b])
+        for j in range(n):
+            row = int(case.cu_q_lens[b]) + j
+            d_out, d_lse = oracle.decode(case.q[row:row + 1], kp, vp, case.block_tables[b:b + 1],
+                                         np.array([L - n + j + 1]), case.scale, case.softcap,
+                                         window, case.dtype)
+            np.testing.assert_allclose(out[row], d_out[0], rtol=0, atol=1e-12)
+            np.testing.assert_allclose(lse[row], d_lse[0], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# P9 shared prefix
+# ---------------------------------------------------------------------------
+def test_p9_shared_prefix_equals_private_copies():
+    case = wl.make_prefill_case(91, [64, 80, 48], [16, 7, 30], 4, 1, 32, "bf16",
+                                shared_prefix_blocks=3)
+    kp, vp = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           case.dtype)
+    a = (case.scale, case.softcap, case.window, case.dtype)
+    out0, lse0 = oracle.prefill(case.q, case.cu_q_lens, kp, vp, case.block_tables,
+                                case.context_lens, *a)
+    # give every sequence after the first its own copy of the shared blocks
+    shared = case.block_tables[0, :3]
+    extra = (case.num_seqs - 1) * 3
+    kp2 = np.concatenate([kp, np.zeros((extra,) + kp.shape[1:], kp.dtype)])
+    vp2 = np.concatenate([vp, np.zeros((extra,) + vp.shape[1:], vp.dtype)])
+    bt2 = case.block_tables.copy()
+    nxt = case.num_blocks
+    for b in range(1, case.num_seqs):
+        for j in range(3):
+            kp2[nxt] = kp[shared[j]]
+            vp2[nxt] = vp[shared[j]]
+            bt2[b, j] = nxt
+            nxt += 1
+    assert len(set(bt2[:, :3].ravel().tolist())) == 3 * case.num_seqs
+    out1, lse1 = oracle.prefill(case.q, case.cu_q_lens, kp2, vp2, bt2, case.context_lens, *a)
+    assert np.array_equal(out0, out1) and np.array_equal(lse0, lse1)
+
+
+# ---------------------------------------------------------------------------
+# P10 append
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_p10_append_round_trip(dtype):
+    case = wl.make_prefill_case(101, [5, 16, 31], [11, 17, 2], 4, 2, 16, dtype)
+    slots = case.slot_mapping.copy()
+    slots[3] = -1  # a padding token: must be skipped
+    kp, vp = oracle.append(case.k_new, case.v_new, slots, case.k_pool, case.v_pool, dtype)
+    X = 16 // wl.elem_bytes(dtype)
+    touched = np.zeros(kp.shape[:1] + kp.shape[3:4], dtype=bool)  # [NB, 16]
+    for i, s in enumerate(slots.tolist()):
+        if s < 0:
+            continue
+        blk, off = divmod(s, 16)
+        touched[blk, off] = True
+        for g in range(case.num_kv_heads):
+            for d in range(case.head_dim):
+                assert kp[blk, g, d // X, off, d % X] == case.k_new[i, g, d]
+                assert vp[blk, g, d, off] == case.v_new[i, g, d]
+    # every other slot is bit-identical (NaN poison included)
+    for blk in range(case.num_blocks):
+        for off in range(16):
+            if not touched[blk, off]:
+                assert np.array_equal(kp[blk, :, :, off, :], case.k_pool[blk, :, :, off, :])
+                assert np.array_equal(vp[blk, :, :, off], case.v_pool[blk, :, :, off])
+    # the skipped token's slot is still NaN
+    blk, off = divmod(int(case.slot_mapping[3]), 16)
+    assert np.isnan(f32vals(vp[blk, :, :, off], dtype)).all()
+    # gathering through the tables returns the appended rows exactly
+    b, n0 = 1, int(case.cu_q_lens[1])
+    K, V = oracle.gather_sequence(kp, vp, case.block_tables[b], int(case.context_lens[b]), 1, dtype)
+    cached = int(case.context_lens[b]) - int(case.q_lens[b])
+    np.testing.assert_array_equal(K[cached:], f32vals(case.k_new[n0:n0 + 17, 1], dtype))
+    np.testing.assert_array_equal(V[cached:], f32vals(case.v_new[n0:n0 + 17, 1], dtype))
+
+
+def test_p10_append_rejects_bad_slots():
+    case = wl.make_prefill_case(102, [3], [4], 2, 1, 16, "bf16")
+    dup = case.slot_mapping.copy()
+    dup[2] = dup[1]
+    with pytest.raises(ValueError):
+        oracle.append(case.k_new, case.v_new, dup, case.k_pool, case.v_pool, "bf16")
+    far = case.slot_mapping.copy()
+    far[0] = case.num_blocks * 16
+    with pytest.raises(ValueError):
+        oracle.append(case.k_new, case.v_new, far, case.k_pool, case.v_pool, "bf16")
+
+
+# ---------------------------------------------------------------------------
+# P11 softcap
+# ---------------------------------------------------------------------------
+def test_p11_softcap_limits():
+    rng = np.random.default_rng(111)
+    q = rng.standard_normal((3, 16)) * 10
+    K = rng.standard_normal((200, 16)) * 10
+    raw = oracle.scores(q, K, 0.25, 0.0)
+    huge = oracle.scores(q, K, 0.25, 1e30)
+    np.testing.assert_allclose(huge, raw, rtol=1e-15, atol=1e-12)
+    for cap in (0.5, 5.0, 50.0):
+        s = oracle.scores(q, K, 0.25, cap)
+        assert (np.abs(s) <= cap).all()
+        order = np.argsort(raw, axis=1)
+        assert (np.diff(np.take_along_axis(s, order, 1), axis=1) >= 0).all()  # monotone
+        small = np.abs(raw) < 1e-2 * cap
+        # cap*tanh(x/cap) = x - x^3/(3 cap^2) + O(x^5)
+        np.testing.assert_allclose(s[small], raw[small] - raw[small] ** 3 / (3 * cap * cap),
+                                   rtol=0, atol=1e-9 * cap)
+        big = np.abs(raw) > 20 * cap
+        np.testing.assert_allclose(np.abs(s[big]), cap, rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# P12 GQA reduction
+# ---------------------------------------------------------------------------
+def test_p12_gqa_equals_replicated_heads():
+    case = wl.make_decode_case(121, [9, 40, 77], 8, 2, 16, "bf16", softcap=2.0)
+    G = case.gqa_group
+    a = (case.scale, case.softcap, case.window, case.dtype)
+    out, lse = oracle.decode(case.q, case.k_pool, case.v_pool, case.block_tables,
+                             case.context_lens, *a)
+    kp = np.repeat(case.k_pool, G, axis=1)  # kv head g copied to q heads g*G .. g*G+G-1
+    vp = np.repeat(case.v_pool, G, axis=1)
+    out1, lse1 = oracle.decode(case.q, kp, vp, case.block_tables, case.context_lens, *a)
+    np.testing.assert_allclose(out1, out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse1, lse, rtol=0, atol=1e-12)
+    # a wrong group mapping (interleaved) would differ
+    perm = np.arange(case.num_q_heads).reshape(2, G).T.ravel()
+    out2, _ = oracle.decode(case.q[:, perm], case.k_pool, case.v_pool, case.block_tables,
+                            case.context_lens, *a)
+    assert not np.allclose(out2[:, perm], out, atol=1e-3)
+
+
+# ---------------------------------------------------------------------------
+# the seeded generators
+# ---------------------------------------------------------------------------
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(131)
+    x = rng.standard_normal(100000).astype(np.float32) * np.float32(3.0)
+    # exact ties: the low 16 bits equal 0x8000
+    ties = (rng.integers(0, 0x7F00, 1000).astype(np.uint32) << 16 | 0x8000).view(np.float32)
+    x = np.concatenate([x, ties, np.array([0.0, -0.0, 1e-40, 3.0e38], np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(wl.to_bits(x, "bf16"), want)
+    assert np.array_equal(wl.bits_to_f32(want, "bf16"),
+                          torch.from_numpy(want.view(np.int16)).view(torch.bfloat16).float().numpy())
+
+
+def test_named_workloads_shapes():
+    c1 = wl.tiny_decode_fp32()
+    assert c1.context_lens.tolist() == [17, 40, 64, 100] and c1.num_blocks == 64
+    assert c1.dtype == "f32" and c1.head_dim == 64 and c1.gqa_group == 4
+    assert c1.k_pool.shape == (64, 1, 16, 16, 4) and c1.v_pool.shape == (64, 1, 64, 16)
+    c2 = wl.gemma_decode()
+    assert c2.num_seqs == 32 and 512 <= c2.context_lens.min() and c2.context_lens.max() <= 4096
+    assert (c2.num_q_heads, c2.num_kv_heads, c2.head_dim, c2.softcap) == (8, 2, 256, 50.0)
+    need = sum((int(L) + 15) // 16 for L in c2.context_lens)
+    assert c2.num_blocks == math.ceil(1.25 * need)
+    c5 = wl.chunked_prefill_shared_prefix()
+    assert (c5.block_tables[:, :64] == c5.block_tables[0, :64]).all()
+    assert len(set(c5.block_tables[:, 64:].ravel().tolist())) == 8 * 96
+    assert c5.num_blocks == 1040 and c5.num_q_tokens == 4096
+    assert (c5.context_lens == 2560).all()
+    blocks = c5.slot_mapping // 16
+    assert not np.isin(blocks, c5.block_tables[0, :64]).any()  # the chunk never writes the prefix
+
+
+def test_poison_marks_exactly_the_invisible_slots():
+    case = wl.make_decode_case(141, [1, 16, 17, 50], 2, 1, 16, "bf16")
+    vals = f32vals(case.v_pool, "bf16")  # [NB, Hkv, D, 16]
+    seen = np.zeros((case.num_blocks, 16), dtype=bool)
+    for b, L in enumerate(case.context_lens.tolist()):
+        for t in range(L):
+            seen[case.block_tables[b, t // 16], t % 16] = True
+    for blk in range(case.num_blocks):
+        for off in range(16):
+            col = vals[blk, :, :, off]
+            assert (np.isfinite(col).all() if seen[blk, off] else np.isnan(col).all())
