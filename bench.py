@@ -1,0 +1,367 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-paged KV attention path on one MI355X.
+
+Headline step (timed): one decode tick of the Gemma-style workload -- 32
+sequences with context lengths uniform in [512, 4096], 8 query / 2 kv heads,
+head_dim 256, bf16, tanh softcap 50: append the tick's 32 new K/V rows into
+their cache slots, then run the paged decode over every sequence.  ``value``
+is algorithmic HBM bytes per second of the whole step (K/V read once per kv
+head, q read, output written, table entries and lengths, the appended rows
+read and written).  The pool is replicated R times in HBM and consecutive
+steps read different replicas, so that no step is served from the 256 MB
+Infinity Cache by its predecessor.
+
+Also reported on the same line: the decode kernel's roofline (HIP-event
+timing of the decode launches inside the timed region), the chunked-prefill
+TFLOP/s (the metric's second half), the other decode workloads, and the CPU
+oracle timed on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+METRIC = "paged-decode KV GB/s (% HBM peak) + tok/s; paged-prefill TFLOP/s at 1 GPU"
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "decode": ["decode.hip", "attn_tile.hpp", "common.hpp", "api.cpp"],
+    "prefill": ["prefill.hip", "attn_tile.hpp", "common.hpp", "api.cpp"],
+}
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--replicas", type=int, default=0, help="pool replicas (0: enough for 1 GiB)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--quick", action="store_true", help="headline step only")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="run only a plain device copy of known size (HBM counter calibration)")
+    return p.parse_args()
+
+
+def source_sha(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "block_paged_kv_append_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str, dispatches_per_launch: int = 1):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, "hbm_counters.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)[kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_sha") != source_sha(kind):
+        return None
+    return rec["bytes_per_dispatch"] * dispatches_per_launch
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work
+# ---------------------------------------------------------------------------
+def decode_bytes(case) -> int:
+    s = 2 if case.dtype == "bf16" else 4
+    B, Hq, Hkv, D = case.num_seqs, case.num_q_heads, case.num_kv_heads, case.head_dim
+    kv = 0
+    blocks = 0
+    for L in case.context_lens.tolist():
+        n_vis = min(L, case.window) if case.window > 0 else L
+        kv += n_vis * Hkv * D * s * 2
+        lo = L - n_vis
+        blocks += ((L - 1) // 16 - lo // 16 + 1) if L > 0 else 0
+    return kv + 2 * B * Hq * D * s + 4 * (B + blocks)
+
+
+def append_bytes(num_tokens, Hkv, D, s) -> int:
+    return 2 * (2 * num_tokens * Hkv * D * s) + 4 * num_tokens
+
+
+def prefill_flops(case) -> float:
+    pairs = 0
+    for b in range(case.num_seqs):
+        L, n = int(case.context_lens[b]), int(case.q_lens[b])
+        for j in range(n):
+            qp = L - n + j
+            lo = max(0, qp - case.window + 1) if case.window > 0 else 0
+            pairs += qp - lo + 1
+    return 4.0 * case.head_dim * case.num_q_heads * pairs
+
+
+# ---------------------------------------------------------------------------
+# GPU side
+# ---------------------------------------------------------------------------
+class DecodeBench:
+    """Device-resident inputs of one decode workload, replicated R times."""
+
+    def __init__(self, case, replicas, torch, pkv):
+        import numpy as np
+
+        self.case, self.torch, self.pkv = case, torch, pkv
+        dt = case.dtype
+        pool_bytes = case.k_pool.nbytes + case.v_pool.nbytes
+        R = replicas or max(2, math.ceil((1 << 30) / pool_bytes))
+        self.R = R
+        kp = pkv.from_bits(case.k_pool, dt)
+        vp = pkv.from_bits(case.v_pool, dt)
+        self.kp = torch.cat([kp] * R).contiguous()
+        self.vp = torch.cat([vp] * R).contiguous()
+        del kp, vp
+        NB = case.num_blocks
+        bt = case.block_tables.astype(np.int64)
+        self.bt = [torch.from_numpy((bt + r * NB).astype(np.int32)).cuda() for r in range(R)]
+        self.cl = torch.from_numpy(case.context_lens).cuda()
+        self.q = pkv.from_bits(case.q, dt)
+        self.out = torch.empty_like(self.q)
+        B, Hkv, D = case.num_seqs, case.num_kv_heads, case.head_dim
+        # this tick's new token of each sequence sits at position L - 1
+        slots = np.array([int(case.block_tables[b, (L - 1) // 16]) * 16 + (L - 1) % 16
+                          for b, L in enumerate(case.context_lens.tolist())], dtype=np.int64)
+        self.slots = [torch.from_numpy((slots + r * NB * 16).astype(np.int32)).cuda()
+                      for r in range(R)]
+        g = torch.Generator(device="cuda")
+        g.manual_seed(12345)
+        tdt = self.q.dtype
+        self.k_new = torch.randn(B, Hkv, D, generator=g, device="cuda").to(tdt)
+        self.v_new = torch.randn(B, Hkv, D, generator=g, device="cuda").to(tdt)
+        ws = pkv.paged_attn_decode_workspace_size(B, Hkv, case.gqa_group, D, case.max_context_len,
+                                                  case.partition_size)
+        self.ws = torch.zeros(ws, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+
+    def decode(self, r):
+        c, pkv = self.case, self.pkv
+        args = (self.out, self.q, self.kp, self.vp, self.bt[r], self.cl, c.max_context_len, c.scale,
+                c.softcap, c.window)
+        if c.partition_size:
+            pkv.paged_attn_decode_splitk(*args, partition_size=c.partition_size, workspace=self.ws)
+        else:
+            pkv.paged_attn_decode(*args, workspace=self.ws)
+
+    def append(self, r):
+        self.pkv.paged_kv_append(self.k_new, self.v_new, self.slots[r], self.kp, self.vp)
+
+
+def time_steps(bench, steps, warmup, with_append, torch):
+    for i in range(warmup):
+        if with_append:
+            bench.append(i % bench.R)
+        bench.decode(i % bench.R)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        r = (warmup + i) % bench.R
+        if with_append:
+            bench.append(r)
+        ev[i][0].record()
+        bench.decode(r)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    return wall, kern_ms
+
+
+def time_prefill(case, iters, warmup, torch, pkv):
+    import numpy as np
+
+    dt = case.dtype
+    kp = pkv.from_bits(case.k_pool, dt)
+    vp = pkv.from_bits(case.v_pool, dt)
+    k_new, v_new = pkv.from_bits(case.k_new, dt), pkv.from_bits(case.v_new, dt)
+    slots = torch.from_numpy(case.slot_mapping).cuda()
+    q = pkv.from_bits(case.q, dt)
+    out = torch.empty_like(q)
+    cu = torch.from_numpy(case.cu_q_lens).cuda()
+    bt = torch.from_numpy(case.block_tables).cuda()
+    cl = torch.from_numpy(case.context_lens).cuda()
+
+    def append():
+        pkv.paged_kv_append(k_new, v_new, slots, kp, vp)
+
+    def prefill():
+        pkv.paged_attn_prefill(out, q, cu, case.max_q_len, kp, vp, bt, cl, case.max_context_len,
+                               case.scale, case.softcap, case.window)
+
+    for _ in range(warmup):
+        append()
+        prefill()
+    torch.cuda.synchronize()
+    ea = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    ep = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    for i in range(iters):
+        ea[i][0].record()
+        append()
+        ea[i][1].record()
+        ep[i][0].record()
+        prefill()
+        ep[i][1].record()
+    torch.cuda.synchronize()
+    return (float(np.mean([a.elapsed_time(b) for a, b in ea])),
+            float(np.mean([a.elapsed_time(b) for a, b in ep])))
+
+
+def calibrate_copy(torch):
+    """A plain device-to-device copy of 1 GiB, 10 times: the reference for
+    scaling the HBM FETCH_SIZE / WRITE_SIZE counters."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(10):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 10}))
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on the host cores
+# ---------------------------------------------------------------------------
+def cpu_baseline(case, budget_s):
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    per_pass = decode_bytes(case)
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode(case.q, case.k_pool, case.v_pool, case.block_tables, case.context_lens,
+                      case.scale, case.softcap, case.window, case.dtype)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or passes >= 1000:
+            break
+    return {"value": round(per_pass * passes / el / 1e9, 4), "unit": "GB/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"full workload (all {case.num_seqs} sequences), {passes} passes in "
+                      f"{el:.1f} s; float64 numpy, BLAS threads {threads}, "
+                      f"host affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+# ---------------------------------------------------------------------------
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(use --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    import block_paged_kv_append_amd as pkv
+    from block_paged_kv_append_amd import workloads as wl
+
+    pkv.load_library()  # raises if libpkv.so is missing: there is no fallback
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
+
+    t_setup = time.perf_counter()
+    case = wl.gemma_decode()
+    bench = DecodeBench(case, args.replicas, torch, pkv)
+    print(f"# setup {time.perf_counter() - t_setup:.1f}s, pool replicas {bench.R}", file=sys.stderr,
+          flush=True)
+
+    wall, kern_ms = time_steps(bench, args.steps, args.warmup, True, torch)
+    ms_per_step = wall * 1e3 / args.steps
+    dbytes = decode_bytes(case)
+    abytes = append_bytes(case.num_seqs, case.num_kv_heads, case.head_dim, 2)
+    value = (dbytes + abytes) / (ms_per_step * 1e-3) / 1e9
+    kern_avg_ms = float(np.mean(kern_ms))
+    achieved = dbytes / (kern_avg_ms * 1e-3) / 1e9
+    traffic = measured_traffic("decode")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "gemma_decode: 32 seqs, ctx U[512,4096], 8q/2kv heads, D256, bf16, "
+                               "softcap 50, block 16; step = append 32 tokens + paged decode",
+                   "num_seqs": case.num_seqs, "context_tokens": int(case.context_lens.sum()),
+                   "pool_replicas": bench.R},
+        "tok_per_s": round(case.num_seqs / (ms_per_step * 1e-3), 1),
+        "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "decode_kernel (balanced split)",
+                     "kernel_ms": round(kern_avg_ms, 5), "algorithmic_bytes": dbytes},
+    }
+
+    if not args.quick:
+        extra = {}
+        pc = wl.chunked_prefill_shared_prefix()
+        app_ms, pre_ms = time_prefill(pc, 20, 3, torch, pkv)
+        flops = prefill_flops(pc)
+        tf = flops / (pre_ms * 1e-3) / 1e12
+        ab = append_bytes(pc.num_q_tokens, pc.num_kv_heads, pc.head_dim, 2)
+        line["prefill"] = {
+            "workload": "chunked_prefill_shared_prefix: 8 seqs x (2048 cached, first 1024 shared) "
+                        "+ 512-token chunk, 8q/2kv heads, D256, bf16, causal",
+            "tflops": round(tf, 2), "ms": round(pre_ms, 5), "flops": flops,
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
+                         "traffic": measured_traffic("prefill")},
+            "append": {"ms": round(app_ms, 5), "gbs": round(ab / (app_ms * 1e-3) / 1e9, 1),
+                       "bytes": ab},
+        }
+        del pc
+        for maker in (wl.sliding_window_decode, wl.long_context_splitk):
+            c = maker()
+            b = DecodeBench(c, 0, torch, pkv)
+            _, km = time_steps(b, 50, 5, False, torch)
+            ms = float(np.mean(km))
+            gbs = decode_bytes(c) / (ms * 1e-3) / 1e9
+            extra[c.name] = {"ms": round(ms, 5), "gbs": round(gbs, 1),
+                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                             "tok_per_s": round(c.num_seqs / (ms * 1e-3), 1),
+                             "entry": "splitk P=%d" % c.partition_size if c.partition_size else "balanced"}
+            del b, c
+            torch.cuda.empty_cache()
+        line["other_workloads"] = extra
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,284 @@
+"""block_paged_kv_append_amd -- attention over a block-paged KV cache on MI355X.
+
+A thin ctypes binding over ``libpkv.so`` (HIP, gfx950), whose C ABI is declared
+in ``include/pkv.h``.  The functions below carry the C entry points' names and
+only marshal arguments: shapes and dtypes are read from torch tensors, device
+pointers and the current HIP stream are passed through, and every step of the
+computation runs in the library's kernels.  There is no fallback: if the
+library is missing, calls raise.
+
+Pool layout (vLLM/PagedAttention), X = 16 bytes / element size:
+    k_pool [num_blocks, num_kv_heads, head_dim // X, 16, X]
+    v_pool [num_blocks, num_kv_heads, head_dim, 16]
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
+
+PKV_F32 = 0
+PKV_BF16 = 1
+BLOCK_SIZE = 16
+
+_STATUS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_EWORKSPACE",
+           -4: "PKV_EHIP"}
+
+# (name, restype, argtypes) of every entry point in include/pkv.h
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "paged_kv_append": (ctypes.c_int, [_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "paged_attn_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
+    "paged_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I,
+                                         _I, _F, _F, _I, _P, _Z, _I, _P]),
+    "paged_attn_decode_splitk": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I,
+                                                _I, _I, _I, _F, _F, _I, _I, _P, _Z, _I, _P]),
+    "paged_attn_prefill": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I,
+                                          _I, _I, _I, _I, _F, _F, _I, _I, _P]),
+    "pkv_last_error": (ctypes.c_char_p, []),
+}
+
+
+class PkvError(RuntimeError):
+    def __init__(self, fn: str, code: int, message: str):
+        super().__init__(f"{fn} failed with {_STATUS.get(code, code)}: {message}")
+        self.code = code
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def load_library(path: Optional[str] = None) -> ctypes.CDLL:
+    """Load libpkv.so (after torch, so that both share torch's HIP runtime)."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None and path is None:
+            return _lib
+        import torch  # noqa: F401  -- torch's libamdhip64 must be the one in use
+
+        p = path or LIB_PATH
+        if not os.path.exists(p):
+            raise RuntimeError(f"{p} is missing: build it with `python -m block_paged_kv_append_amd.build`")
+        lib = ctypes.CDLL(p)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        if path is None:
+            _lib = lib
+        return lib
+
+
+def pkv_last_error() -> str:
+    return load_library().pkv_last_error().decode()
+
+
+def _check(fn: str, rc: int) -> None:
+    if rc != 0:
+        raise PkvError(fn, rc, pkv_last_error())
+
+
+# ---------------------------------------------------------------------------
+# tensor marshalling
+# ---------------------------------------------------------------------------
+def _dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.bfloat16:
+        return PKV_BF16
+    if t.dtype == torch.float32:
+        return PKV_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _i32(t, name):
+    import torch
+
+    if t.dtype != torch.int32:
+        raise TypeError(f"{name} must be int32, got {t.dtype}")
+    return _ptr(t)
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream or None
+
+
+def _pool_dims(k_pool, v_pool):
+    nb, hkv, d, bs = v_pool.shape
+    if bs != BLOCK_SIZE:
+        raise ValueError(f"v_pool's last dim must be {BLOCK_SIZE}")
+    x = 16 // v_pool.element_size()
+    if tuple(k_pool.shape) != (nb, hkv, d // x, BLOCK_SIZE, x):
+        raise ValueError(f"k_pool shape {tuple(k_pool.shape)} does not match v_pool {tuple(v_pool.shape)}")
+    if k_pool.dtype != v_pool.dtype:
+        raise TypeError("k_pool and v_pool dtypes differ")
+    return nb, hkv, d
+
+
+# ---------------------------------------------------------------------------
+# entry points
+# ---------------------------------------------------------------------------
+def paged_kv_append(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None) -> None:
+    """Write rows ``k_new/v_new [T, Hkv, D]`` to slots ``slot_mapping [T]``."""
+    nb, hkv, d = _pool_dims(k_pool, v_pool)
+    T = k_new.shape[0]
+    if tuple(k_new.shape) != (T, hkv, d) or tuple(v_new.shape) != (T, hkv, d):
+        raise ValueError("k_new/v_new must be [T, num_kv_heads, head_dim]")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise TypeError("k_new/v_new dtype must match the pools")
+    if slot_mapping.numel() != T:
+        raise ValueError("slot_mapping must have T entries")
+    lib = load_library()
+    rc = lib.paged_kv_append(_ptr(k_new), _ptr(v_new), _i32(slot_mapping, "slot_mapping"), T,
+                             _ptr(k_pool), _ptr(v_pool), nb, hkv, d, BLOCK_SIZE,
+                             _dtype_code(k_pool), _stream(stream))
+    _check("paged_kv_append", rc)
+
+
+def paged_attn_decode_workspace_size(num_seqs, num_kv_heads, gqa_group, head_dim,
+                                     max_context_len, partition_size=0) -> int:
+    return int(load_library().paged_attn_decode_workspace_size(
+        num_seqs, num_kv_heads, gqa_group, head_dim, max_context_len, partition_size))
+
+
+_ws_cache = {}
+_ws_lock = threading.Lock()
+
+
+def decode_workspace(nbytes: int, device, stream=None):
+    """A zero-initialised workspace of at least ``nbytes``, cached per device and
+    stream (the library leaves its counters zero after every call)."""
+    import torch
+
+    key = (str(device), _stream(stream))
+    with _ws_lock:
+        ws = _ws_cache.get(key)
+        if ws is None or ws.numel() < nbytes:
+            ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+            _ws_cache[key] = ws
+        return ws
+
+
+def _decode_dims(out, q, k_pool, v_pool, block_tables, context_lens):
+    nb, hkv, d = _pool_dims(k_pool, v_pool)
+    B, hq, dq = q.shape
+    if dq != d or hq % hkv:
+        raise ValueError(f"q shape {tuple(q.shape)} does not fit pools with {hkv} kv heads of {d}")
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or q.dtype != k_pool.dtype:
+        raise ValueError("out must match q, and q's dtype the pools'")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or context_lens.numel() != B:
+        raise ValueError("block_tables [B, MB] and context_lens [B] must match q's batch")
+    return nb, hkv, d, B, hq // hkv, block_tables.shape[1]
+
+
+def paged_attn_decode(out, q, k_pool, v_pool, block_tables, context_lens, max_context_len,
+                      scale, softcap=0.0, window=0, lse=None, workspace=None, stream=None) -> None:
+    """One-token decode for every sequence; writes ``out [B, Hq, D]`` (and ``lse``)."""
+    nb, hkv, d, B, G, MB = _decode_dims(out, q, k_pool, v_pool, block_tables, context_lens)
+    need = paged_attn_decode_workspace_size(B, hkv, G, d, max_context_len, 0)
+    ws = workspace if workspace is not None else decode_workspace(need, q.device, stream)
+    lib = load_library()
+    rc = lib.paged_attn_decode(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool), nb,
+                               _i32(block_tables, "block_tables"), MB,
+                               _i32(context_lens, "context_lens"), int(max_context_len), B, hkv,
+                               G, d, BLOCK_SIZE, float(scale), float(softcap), int(window),
+                               _ptr(ws), ws.numel() * ws.element_size(), _dtype_code(q),
+                               _stream(stream))
+    _check("paged_attn_decode", rc)
+
+
+def paged_attn_decode_splitk(out, q, k_pool, v_pool, block_tables, context_lens,
+                             max_context_len, scale, softcap=0.0, window=0, partition_size=512,
+                             lse=None, workspace=None, stream=None) -> None:
+    """Split-K decode with fixed ``partition_size``-token partitions merged by log-sum-exp."""
+    nb, hkv, d, B, G, MB = _decode_dims(out, q, k_pool, v_pool, block_tables, context_lens)
+    need = paged_attn_decode_workspace_size(B, hkv, G, d, max_context_len, partition_size)
+    ws = workspace if workspace is not None else decode_workspace(need, q.device, stream)
+    lib = load_library()
+    rc = lib.paged_attn_decode_splitk(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                      nb, _i32(block_tables, "block_tables"), MB,
+                                      _i32(context_lens, "context_lens"), int(max_context_len), B,
+                                      hkv, G, d, BLOCK_SIZE, float(scale), float(softcap),
+                                      int(window), int(partition_size), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _dtype_code(q),
+                                      _stream(stream))
+    _check("paged_attn_decode_splitk", rc)
+
+
+def paged_attn_prefill(out, q, cu_q_lens, max_q_len, k_pool, v_pool, block_tables, context_lens,
+                       max_context_len, scale, softcap=0.0, window=0, lse=None,
+                       stream=None) -> None:
+    """Causal attention of the chunk rows ``q [Tq, Hq, D]`` over prefix + chunk."""
+    nb, hkv, d = _pool_dims(k_pool, v_pool)
+    Tq, hq, dq = q.shape
+    if dq != d or hq % hkv:
+        raise ValueError(f"q shape {tuple(q.shape)} does not fit the pools")
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or q.dtype != k_pool.dtype:
+        raise ValueError("out must match q, and q's dtype the pools'")
+    B = context_lens.numel()
+    if cu_q_lens.numel() != B + 1 or block_tables.shape[0] != B:
+        raise ValueError("cu_q_lens [B+1], block_tables [B, MB], context_lens [B] disagree")
+    lib = load_library()
+    rc = lib.paged_attn_prefill(_ptr(out), _ptr(lse), _ptr(q), _i32(cu_q_lens, "cu_q_lens"), Tq,
+                                int(max_q_len), _ptr(k_pool), _ptr(v_pool), nb,
+                                _i32(block_tables, "block_tables"), block_tables.shape[1],
+                                _i32(context_lens, "context_lens"), int(max_context_len), B, hkv,
+                                hq // hkv, d, BLOCK_SIZE, float(scale), float(softcap),
+                                int(window), _dtype_code(q), _stream(stream))
+    _check("paged_attn_prefill", rc)
+
+
+# ---------------------------------------------------------------------------
+# numpy bit arrays <-> device tensors
+# ---------------------------------------------------------------------------
+def from_bits(bits, dtype: str, device="cuda"):
+    """uint16 (bf16) / uint32 (fp32) storage bits -> a device tensor."""
+    import numpy as np
+    import torch
+
+    if dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    elif dtype == "f32":
+        t = torch.from_numpy(np.ascontiguousarray(bits).view(np.float32))
+    else:
+        raise ValueError(dtype)
+    return t.to(device)
+
+
+def to_bits(t):
+    """device tensor -> numpy storage bits (uint16 for bf16, uint32 for fp32)."""
+    import numpy as np
+    import torch
+
+    c = t.detach().contiguous().cpu()
+    if c.dtype == torch.bfloat16:
+        return c.view(torch.int16).numpy().view(np.uint16)
+    if c.dtype == torch.float32:
+        return c.numpy().view(np.uint32)
+    raise TypeError(c.dtype)
+
+
+__all__ = [
+    "PKV_F32", "PKV_BF16", "BLOCK_SIZE", "PkvError", "SIGNATURES", "load_library",
+    "pkv_last_error", "paged_kv_append", "paged_attn_decode_workspace_size",
+    "paged_attn_decode", "paged_attn_decode_splitk", "paged_attn_prefill", "decode_workspace",
+    "from_bits", "to_bits",
+]

@@ -1,0 +1,335 @@
+// C ABI of libpkv: argument validation, workspace geometry and launches.
+// The operations and their conventions are documented in include/pkv.h.
+#include "pkv.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "launch.hpp"
+
+// Tuning of the balanced decode split (compile-time; see the decode kernel).
+#ifndef PKV_DECODE_WGS_PER_CU
+#define PKV_DECODE_WGS_PER_CU 2
+#endif
+#ifndef PKV_DECODE_MIN_BLOCKS_PER_WG
+#define PKV_DECODE_MIN_BLOCKS_PER_WG 8
+#endif
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return PKV_OK;
+  return fail(PKV_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int elem_bytes(int32_t dtype) {
+  switch (dtype) {
+    case PKV_F32: return 4;
+    case PKV_BF16: return 2;
+    default: return 0;
+  }
+}
+
+bool head_dim_ok(int32_t d) { return d == 64 || d == 128 || d == 256; }
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int cu_count(int* out) {
+  static int cache[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+  if (dev >= 0 && dev < 64 && cache[dev] > 0) {
+    *out = cache[dev];
+    return PKV_OK;
+  }
+  int n = 0;
+  e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return from_hip(e, "hipDeviceGetAttribute");
+  if (n <= 0) n = 1;
+  if (dev >= 0 && dev < 64) cache[dev] = n;
+  *out = n;
+  return PKV_OK;
+}
+
+// Checks shared by the attention entry points.
+int check_common(const char* fn, const void* out, const float* lse, const void* q,
+                 const void* k_pool, const void* v_pool, int32_t num_blocks,
+                 const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                 int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim, int32_t block_size,
+                 float scale, float softcap, int32_t dtype) {
+  if (num_seqs < 0) return fail(PKV_EINVAL, "%s: num_seqs %d < 0", fn, num_seqs);
+  if (elem_bytes(dtype) == 0) return fail(PKV_EUNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (!head_dim_ok(head_dim))
+    return fail(PKV_EUNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, head_dim);
+  if (block_size != PKV_BLOCK_SIZE)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size %d, only 16 is supported", fn, block_size);
+  if (gqa_group < 1 || gqa_group > 16)
+    return fail(PKV_EUNSUPPORTED, "%s: gqa_group %d outside 1..16", fn, gqa_group);
+  if (num_kv_heads < 1) return fail(PKV_EINVAL, "%s: num_kv_heads %d < 1", fn, num_kv_heads);
+  if (num_blocks < 1) return fail(PKV_EINVAL, "%s: num_blocks %d < 1", fn, num_blocks);
+  if (max_blocks_per_seq < 1)
+    return fail(PKV_EINVAL, "%s: max_blocks_per_seq %d < 1", fn, max_blocks_per_seq);
+  if ((long long)num_blocks * num_kv_heads * head_dim * PKV_BLOCK_SIZE > (1LL << 40))
+    return fail(PKV_EINVAL, "%s: pool of %d blocks too large", fn, num_blocks);
+  if (max_context_len < 0 || (long long)max_context_len > (long long)max_blocks_per_seq * PKV_BLOCK_SIZE)
+    return fail(PKV_EINVAL, "%s: max_context_len %d outside [0, max_blocks_per_seq * 16 = %lld]",
+                fn, max_context_len, (long long)max_blocks_per_seq * PKV_BLOCK_SIZE);
+  if (!std::isfinite(scale)) return fail(PKV_EINVAL, "%s: scale is not finite", fn);
+  if (std::isnan(softcap) || std::isinf(softcap))
+    return fail(PKV_EINVAL, "%s: softcap is not finite", fn);
+  if (num_seqs == 0) return PKV_OK;
+  if (!out || !q || !k_pool || !v_pool || !block_tables || !context_lens)
+    return fail(PKV_EINVAL, "%s: null array argument", fn);
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(block_tables, 4) || !aligned(context_lens, 4) || (lse && !aligned(lse, 4)))
+    return fail(PKV_EINVAL, "%s: misaligned pointer (arrays need 16-byte alignment)", fn);
+  return PKV_OK;
+}
+
+long long max_units_per_seq(int32_t max_context_len, int32_t window) {
+  long long n = (max_context_len + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
+  if (window > 0) {
+    const long long w = (window + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE + 1;
+    if (w < n) n = w;
+  }
+  return n;
+}
+
+int decode_impl(const char* fn, void* out, float* lse, const void* q, const void* k_pool,
+                const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
+                int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
+                int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                int32_t block_size, float scale, float softcap, int32_t window,
+                int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
+                hipStream_t stream) {
+  int rc = check_common(fn, out, lse, q, k_pool, v_pool, num_blocks, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
+                        gqa_group, head_dim, block_size, scale, softcap, dtype);
+  if (rc != PKV_OK) return rc;
+  if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: partition_size %d is not a multiple of 16", fn,
+                partition_size);
+  if (num_seqs == 0) return PKV_OK;
+  const size_t need = pkv::decode_workspace_bytes(num_seqs, num_kv_heads, gqa_group, head_dim,
+                                                  max_context_len, partition_size);
+  if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
+    return fail(PKV_EWORKSPACE, "%s: workspace of %zu bytes at %p; need %zu bytes, 256-aligned",
+                fn, workspace_bytes, workspace, need);
+
+  pkv::DecodeArgs a{};
+  a.out = out;
+  a.lse = lse;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.max_context_len = max_context_len;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.gqa_group = gqa_group;
+  a.window = window > 0 ? window : 0;
+  a.scale = scale;
+  a.softcap = softcap > 0.f ? softcap : 0.f;
+
+  const size_t slots =
+      pkv::decode_num_slots(num_seqs, num_kv_heads, max_context_len, partition_size);
+  char* base = static_cast<char*>(workspace);
+  a.counters = reinterpret_cast<int32_t*>(base);
+  base += align256((size_t)num_seqs * num_kv_heads * sizeof(int32_t));
+  a.part_o = reinterpret_cast<float*>(base);
+  base += align256(slots * gqa_group * head_dim * sizeof(float));
+  a.part_ml = reinterpret_cast<float*>(base);
+
+  if (partition_size > 0) {
+    const int np = (max_context_len + partition_size - 1) / partition_size;
+    const long long grid = (long long)num_seqs * num_kv_heads * (np > 0 ? np : 1);
+    if (grid > INT_MAX) return fail(PKV_EINVAL, "%s: %lld partitions exceed the grid limit", fn, grid);
+    a.part_blocks = partition_size / PKV_BLOCK_SIZE;
+    a.num_partitions = np > 0 ? np : 1;
+    a.num_workers = (int32_t)grid;
+  } else {
+    int cus = 0;
+    rc = cu_count(&cus);
+    if (rc != PKV_OK) return rc;
+    const long long units = (long long)num_seqs * num_kv_heads *
+                            max_units_per_seq(max_context_len, window);
+    long long n = (units + PKV_DECODE_MIN_BLOCKS_PER_WG - 1) / PKV_DECODE_MIN_BLOCKS_PER_WG;
+    const long long cap = (long long)cus * PKV_DECODE_WGS_PER_CU;
+    if (n > cap) n = cap;
+    if (n > pkv::kMaxWorkers) n = pkv::kMaxWorkers;
+    if (n < 1) n = 1;
+    a.part_blocks = 0;
+    a.num_partitions = 0;
+    a.num_workers = (int32_t)n;
+  }
+  return from_hip(pkv::launch_decode(a, head_dim, dtype == PKV_BF16, stream), fn);
+}
+
+}  // namespace
+
+namespace pkv {
+
+size_t decode_num_slots(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                        int32_t partition_size) {
+  if (partition_size == 0) return 2 * (size_t)kMaxWorkers;
+  const long long np = (max_context_len + partition_size - 1) / partition_size;
+  return (size_t)num_seqs * num_kv_heads * (size_t)(np > 0 ? np : 1);
+}
+
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                              int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
+  const size_t slots = decode_num_slots(num_seqs, num_kv_heads, max_context_len, partition_size);
+  return align256((size_t)num_seqs * num_kv_heads * sizeof(int32_t)) +
+         align256(slots * gqa_group * head_dim * sizeof(float)) +
+         align256(slots * gqa_group * 2 * sizeof(float));
+}
+
+}  // namespace pkv
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_err; }
+
+int paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                    int32_t num_tokens, void* k_pool, void* v_pool, int32_t num_blocks,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                    struct ihipStream_t* stream) {
+  const char* fn = "paged_kv_append";
+  if (num_tokens < 0) return fail(PKV_EINVAL, "%s: num_tokens %d < 0", fn, num_tokens);
+  const int es = elem_bytes(dtype);
+  if (es == 0) return fail(PKV_EUNSUPPORTED, "%s: unknown dtype %d", fn, dtype);
+  if (!head_dim_ok(head_dim))
+    return fail(PKV_EUNSUPPORTED, "%s: head_dim %d not in {64, 128, 256}", fn, head_dim);
+  if (block_size != PKV_BLOCK_SIZE)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size %d, only 16 is supported", fn, block_size);
+  if (num_kv_heads < 1) return fail(PKV_EINVAL, "%s: num_kv_heads %d < 1", fn, num_kv_heads);
+  if (num_blocks < 1) return fail(PKV_EINVAL, "%s: num_blocks %d < 1", fn, num_blocks);
+  if ((long long)num_blocks * PKV_BLOCK_SIZE > INT_MAX)
+    return fail(PKV_EINVAL, "%s: %d blocks overflow the int32 slot range", fn, num_blocks);
+  if (num_tokens == 0) return PKV_OK;
+  if (!k_new || !v_new || !slot_mapping || !k_pool || !v_pool)
+    return fail(PKV_EINVAL, "%s: null array argument", fn);
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(slot_mapping, 4))
+    return fail(PKV_EINVAL, "%s: misaligned pointer (arrays need 16-byte alignment)", fn);
+  pkv::AppendArgs a{k_new, v_new, slot_mapping, k_pool, v_pool, num_tokens, num_blocks,
+                    num_kv_heads, head_dim, es};
+  return from_hip(pkv::launch_append(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
+                                        int32_t gqa_group, int32_t head_dim,
+                                        int32_t max_context_len, int32_t partition_size) {
+  if (num_seqs < 0 || num_kv_heads < 1 || gqa_group < 1 || gqa_group > 16 ||
+      !head_dim_ok(head_dim) || max_context_len < 0 || partition_size < 0 ||
+      partition_size % PKV_BLOCK_SIZE != 0)
+    return 0;
+  return pkv::decode_workspace_bytes(num_seqs, num_kv_heads, gqa_group, head_dim, max_context_len,
+                                     partition_size);
+}
+
+int paged_attn_decode(void* out, float* lse, const void* q, const void* k_pool,
+                      const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, int32_t num_seqs, int32_t num_kv_heads,
+                      int32_t gqa_group, int32_t head_dim, int32_t block_size, float scale,
+                      float softcap, int32_t window, void* workspace, size_t workspace_bytes,
+                      int32_t dtype, struct ihipStream_t* stream) {
+  return decode_impl("paged_attn_decode", out, lse, q, k_pool, v_pool, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
+                     gqa_group, head_dim, block_size, scale, softcap, window, 0, workspace,
+                     workspace_bytes, dtype, reinterpret_cast<hipStream_t>(stream));
+}
+
+int paged_attn_decode_splitk(void* out, float* lse, const void* q, const void* k_pool,
+                             const void* v_pool, int32_t num_blocks,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t max_context_len,
+                             int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                             int32_t head_dim, int32_t block_size, float scale, float softcap,
+                             int32_t window, int32_t partition_size, void* workspace,
+                             size_t workspace_bytes, int32_t dtype, struct ihipStream_t* stream) {
+  if (partition_size <= 0 || partition_size % PKV_BLOCK_SIZE != 0)
+    return fail(PKV_EUNSUPPORTED, "paged_attn_decode_splitk: partition_size %d is not a positive "
+                "multiple of 16", partition_size);
+  return decode_impl("paged_attn_decode_splitk", out, lse, q, k_pool, v_pool, num_blocks,
+                     block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
+                     num_kv_heads, gqa_group, head_dim, block_size, scale, softcap, window,
+                     partition_size, workspace, workspace_bytes, dtype,
+                     reinterpret_cast<hipStream_t>(stream));
+}
+
+int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q_lens,
+                       int32_t num_q_tokens, int32_t max_q_len, const void* k_pool,
+                       const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t max_context_len, int32_t num_seqs, int32_t num_kv_heads,
+                       int32_t gqa_group, int32_t head_dim, int32_t block_size, float scale,
+                       float softcap, int32_t window, int32_t dtype, struct ihipStream_t* stream) {
+  const char* fn = "paged_attn_prefill";
+  int rc = check_common(fn, out, lse, q, k_pool, v_pool, num_blocks, block_tables,
+                        max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
+                        gqa_group, head_dim, block_size, scale, softcap, dtype);
+  if (rc != PKV_OK) return rc;
+  if (16 % gqa_group != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: gqa_group %d must divide 16", fn, gqa_group);
+  if (num_q_tokens < 0 || max_q_len < 0)
+    return fail(PKV_EINVAL, "%s: num_q_tokens %d / max_q_len %d < 0", fn, num_q_tokens, max_q_len);
+  if (max_q_len > max_context_len)
+    return fail(PKV_EINVAL, "%s: max_q_len %d > max_context_len %d", fn, max_q_len,
+                max_context_len);
+  if (num_seqs == 0 || num_q_tokens == 0 || max_q_len == 0) return PKV_OK;
+  if (!cu_q_lens || !aligned(cu_q_lens, 4))
+    return fail(PKV_EINVAL, "%s: cu_q_lens null or misaligned", fn);
+
+  pkv::PrefillArgs a{};
+  a.out = out;
+  a.lse = lse;
+  a.q = q;
+  a.cu_q_lens = cu_q_lens;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_tables = block_tables;
+  a.context_lens = context_lens;
+  a.num_q_tokens = num_q_tokens;
+  a.num_blocks = num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.num_seqs = num_seqs;
+  a.num_kv_heads = num_kv_heads;
+  a.gqa_group = gqa_group;
+  a.window = window > 0 ? window : 0;
+  a.scale = scale;
+  a.softcap = softcap > 0.f ? softcap : 0.f;
+  const int per_item = 4 * pkv::prefill_row_tiles(head_dim) * (16 / gqa_group);
+  a.tiles_per_seq = (max_q_len + per_item - 1) / per_item;
+  const long long items = (long long)num_seqs * num_kv_heads * a.tiles_per_seq;
+  if (items > INT_MAX) return fail(PKV_EINVAL, "%s: %lld work items exceed the grid limit", fn, items);
+  a.num_items = (int32_t)items;
+  return from_hip(pkv::launch_prefill(a, head_dim, dtype == PKV_BF16,
+                                      reinterpret_cast<hipStream_t>(stream)),
+                  fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Slot-mapped K/V append into the block pool.
+//
+// Every new token's K and V rows are copied, bit for bit, into the slot the
+// host reserved for it (block-paged KV cache: page "Inference Server",
+// section "The engine"; pool in the vLLM/PagedAttention layout: GitHub
+// README, section "What's inside").
+//
+// One workgroup moves a tile of 16 consecutive tokens of one kv head.  Rows
+// are read with coalesced 16-byte loads into LDS, then written out with the
+// token index fastest across lanes, which is the contiguous direction of both
+// pools: K chunks [.., 16, X] and V rows [.., D, 16].  When the 16 tokens fill
+// consecutive slots of one block (a prefill chunk) each wave writes whole
+// contiguous runs.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace pkv {
+namespace {
+
+constexpr int kAppendThreads = 256;
+
+template <int ES, int D>
+__global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
+  constexpr int X = 16 / ES;           // elements per 16-byte chunk
+  constexpr int NCH = D / X;           // chunks per row
+  constexpr int PITCH = NCH + 1;       // LDS row pitch in chunks (bank-conflict padding)
+  __shared__ u32x4 k_tile[kBlock * PITCH];
+  __shared__ u32x4 v_tile[kBlock * PITCH];
+  __shared__ int slot_of[kBlock];
+
+  const int tid = threadIdx.x;
+  const int g = blockIdx.y;
+  const int Hkv = a.num_kv_heads;
+  const int i0 = blockIdx.x * kBlock;
+  const int nt = min(kBlock, a.num_tokens - i0);
+  const long long nslots = (long long)a.num_blocks * kBlock;
+
+  if (tid < kBlock) {
+    int s = -1;
+    if (tid < nt) {
+      s = a.slot_mapping[i0 + tid];
+      if (s < 0 || (long long)s >= nslots) s = -1;
+    }
+    slot_of[tid] = s;
+  }
+
+  const u32x4* kn = reinterpret_cast<const u32x4*>(a.k_new);
+  const u32x4* vn = reinterpret_cast<const u32x4*>(a.v_new);
+  for (int idx = tid; idx < nt * NCH; idx += kAppendThreads) {
+    const int t = idx / NCH, c = idx % NCH;
+    const size_t row = ((size_t)(i0 + t) * Hkv + g) * NCH;
+    k_tile[t * PITCH + c] = kn[row + c];
+    v_tile[t * PITCH + c] = vn[row + c];
+  }
+  __syncthreads();
+
+  // K: chunk c of token t -> k_pool[blk, g, c, off, :]
+  u32x4* kp = reinterpret_cast<u32x4*>(a.k_pool);
+  for (int idx = tid; idx < kBlock * NCH; idx += kAppendThreads) {
+    const int t = idx % kBlock, c = idx / kBlock;
+    const int s = slot_of[t];
+    if (s < 0) continue;
+    const int blk = s / kBlock, off = s % kBlock;
+    kp[(((size_t)blk * Hkv + g) * NCH + c) * kBlock + off] = k_tile[t * PITCH + c];
+  }
+
+  // V: element d of token t -> v_pool[blk, g, d, off]
+  for (int idx = tid; idx < kBlock * D; idx += kAppendThreads) {
+    const int t = idx % kBlock, d = idx / kBlock;
+    const int s = slot_of[t];
+    if (s < 0) continue;
+    const int blk = s / kBlock, off = s % kBlock;
+    const size_t dst = (((size_t)blk * Hkv + g) * D + d) * kBlock + off;
+    const char* src = reinterpret_cast<const char*>(&v_tile[t * PITCH]) + (size_t)d * ES;
+    if constexpr (ES == 2) {
+      reinterpret_cast<uint16_t*>(a.v_pool)[dst] = *reinterpret_cast<const uint16_t*>(src);
+    } else {
+      reinterpret_cast<uint32_t*>(a.v_pool)[dst] = *reinterpret_cast<const uint32_t*>(src);
+    }
+  }
+}
+
+template <int ES>
+hipError_t launch_es(const AppendArgs& a, hipStream_t stream) {
+  const dim3 grid((a.num_tokens + kBlock - 1) / kBlock, a.num_kv_heads);
+  switch (a.head_dim) {
+    case 64: append_kernel<ES, 64><<<grid, kAppendThreads, 0, stream>>>(a); break;
+    case 128: append_kernel<ES, 128><<<grid, kAppendThreads, 0, stream>>>(a); break;
+    case 256: append_kernel<ES, 256><<<grid, kAppendThreads, 0, stream>>>(a); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream) {
+  if (a.num_tokens <= 0) return hipSuccess;
+  return a.elem_bytes == 2 ? launch_es<2>(a, stream) : launch_es<4>(a, stream);
+}
+
+}  // namespace pkv

@@ -1,0 +1,103 @@
+// Device helpers shared by the libpkv kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pkv {
+
+constexpr int kBlock = 16;  // tokens per cache block
+constexpr int kWave = 64;   // CDNA wavefront
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// matrix-core operations (operand layouts, lane = 16 * j + c):
+//   16x16x32 bf16: A lane holds A[m = c][k = 8j .. 8j+7], B lane holds
+//                  B[k = 8j .. 8j+7][n = c]; C lane holds C[m = 4j + r][n = c].
+//   16x16x16 bf16: as above with k = 4j .. 4j+3.
+//   16x16x4  f32 : A[m = c][k = j], B[k = j][n = c].
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ f32x4 mma_bf16_k32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_bf16_k16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
+                                                    __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mma_f32_k4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------------------
+// scalar math
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// cap * tanh(x / cap), scaled by log2(e) for the base-2 softmax.
+// tanh(y) = 1 - 2 / (e^{2y} + 1): saturates to +-1 when e^{2y} over/underflows.
+__device__ __forceinline__ float softcap_log2(float x, float cap, float inv_cap) {
+  const float e = fast_exp2(x * inv_cap * (2.0f * kLog2e));
+  const float th = 1.0f - 2.0f * fast_rcp(e + 1.0f);
+  return (cap * kLog2e) * th;
+}
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// ---------------------------------------------------------------------------
+// wave reductions / scans
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ long long wave_sum_i64(long long v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ long long wave_incl_scan_i64(long long v, int lane) {
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const long long t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// sequence geometry: the visible token range [vis_lo, L) and the cache
+// blocks it touches, first_blk .. first_blk + nb - 1.
+// ---------------------------------------------------------------------------
+struct SeqSpan {
+  int L;          // context length, clamped to [0, max_len]
+  int vis_lo;     // first visible token (window), 0 without a window
+  int first_blk;  // logical block holding vis_lo
+  int nb;         // number of logical blocks the visible range touches
+};
+
+// max_len: the largest length the caller promised (and the block table can hold)
+__device__ __forceinline__ SeqSpan seq_span(int L_raw, int window, int max_len) {
+  SeqSpan s;
+  s.L = min(max(L_raw, 0), max_len);
+  s.vis_lo = (window > 0) ? max(0, s.L - window) : 0;
+  s.first_blk = s.vis_lo / kBlock;
+  s.nb = (s.L > 0) ? (s.L - 1) / kBlock - s.first_blk + 1 : 0;
+  return s;
+}
+
+}  // namespace pkv

@@ -1,0 +1,88 @@
+// Internal interface between the C-ABI layer (api.cpp) and the kernel
+// translation units.  Arguments here are already validated.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pkv {
+
+struct AppendArgs {
+  const void* k_new;
+  const void* v_new;
+  const int32_t* slot_mapping;
+  void* k_pool;
+  void* v_pool;
+  int32_t num_tokens;
+  int32_t num_blocks;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t elem_bytes;  // 2 (bf16) or 4 (fp32)
+};
+
+struct DecodeArgs {
+  void* out;
+  float* lse;  // may be null
+  const void* q;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t max_context_len;  // lengths are clamped to min(this, max_blocks_per_seq * 16)
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t gqa_group;
+  int32_t window;
+  float scale;
+  float softcap;  // <= 0: off
+  // workspace views
+  int32_t* counters;  // [num_seqs * num_kv_heads], zero between calls
+  float* part_o;      // [num_slots, gqa_group, head_dim]
+  float* part_ml;     // [num_slots, gqa_group, 2]  (max logit in log2 units, sum of 2^(s-m))
+  // work decomposition
+  int32_t num_workers;      // grid size
+  int32_t part_blocks;      // 0: balanced split of all blocks; > 0: fixed partitions of this many blocks
+  int32_t num_partitions;   // fixed partitions per sequence
+};
+
+struct PrefillArgs {
+  void* out;
+  float* lse;  // may be null
+  const void* q;
+  const int32_t* cu_q_lens;
+  const void* k_pool;
+  const void* v_pool;
+  const int32_t* block_tables;
+  const int32_t* context_lens;
+  int32_t num_q_tokens;
+  int32_t num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t num_seqs;
+  int32_t num_kv_heads;
+  int32_t gqa_group;
+  int32_t window;
+  float scale;
+  float softcap;
+  int32_t tiles_per_seq;  // work items per (sequence, kv head)
+  int32_t num_items;      // grid size
+};
+
+// Decode workspace geometry: counters first (256-byte aligned), then the
+// partial outputs, then the (max, sum) pairs.
+constexpr int kMaxWorkers = 1024;  // balanced split: at most this many workgroups
+size_t decode_num_slots(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                        int32_t partition_size);
+size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                              int32_t head_dim, int32_t max_context_len, int32_t partition_size);
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, hipStream_t stream);
+
+// Row tiles (of 16 GQA-packed query rows) per wave in the prefill kernel.
+int prefill_row_tiles(int head_dim);
+
+}  // namespace pkv

@@ -54,9 +54,13 @@ def to_bits(x: np.ndarray, dtype: str) -> np.ndarray:
     x = np.ascontiguousarray(x, dtype=np.float32)
     if dtype == "f32":
         return x.view(np.uint32).copy()
-    u = x.view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
-    return rounded.astype(np.uint16)
+    u = x.view(np.uint32)
+    # finite inputs: u + 0x8000 stays below 2**32, so uint32 arithmetic is exact
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += np.uint32(0x7FFF)
+    r += u
+    r >>= np.uint32(16)
+    return r.astype(np.uint16)
 
 
 def bits_to_f32(bits: np.ndarray, dtype: str) -> np.ndarray:
@@ -70,11 +74,24 @@ def nan_bits(dtype: str):
     return F32_NAN if dtype == "f32" else BF16_NAN
 
 
+_CHUNK = 1 << 22
+
+
 def _normal_bits(rng: np.random.Generator, shape, dtype: str, scale: float = 1.0) -> np.ndarray:
-    x = rng.standard_normal(size=shape, dtype=np.float32)
-    if scale != 1.0:
-        x *= np.float32(scale)
-    return to_bits(x, dtype)
+    """``standard_normal`` float32 draws (times ``scale``) as storage bits, drawn
+    in consecutive chunks into one output array (same stream order as a single
+    draw; avoids large temporaries)."""
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.uint16 if dtype == "bf16" else np.uint32)
+    work = np.empty(min(n, _CHUNK), dtype=np.float32)
+    for lo in range(0, n, _CHUNK):
+        hi = min(n, lo + _CHUNK)
+        x = work[: hi - lo]
+        rng.standard_normal(out=x, dtype=np.float32)
+        if scale != 1.0:
+            x *= np.float32(scale)
+        out[lo:hi] = to_bits(x, dtype)
+    return out.reshape(shape)
 
 
 # --------------------------------------------------------------------------

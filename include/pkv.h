@@ -1,0 +1,193 @@
+/*
+ * pkv.h -- C ABI of libpkv, attention over a block-paged KV cache on AMD
+ * Instinct MI355X (gfx950).
+ *
+ * The operations are those of a single-GPU continuous-batching inference
+ * engine described on the pages "Inference Server" (project README mirror,
+ * section "The engine"; GitHub README, section "What's inside") and
+ * "Inference Server -- Architecture Map" (section "How a single request flows
+ * through the system"):
+ *   - a block-paged, per-layer K/V cache in the vLLM/PagedAttention layout,
+ *     with refcounted (shared) blocks and window-aware sliding layers;
+ *   - paged decode and prefill attention reading K/V through per-sequence
+ *     block tables, with a split-K decode variant;
+ *   - chunked prefill: a chunk of new tokens is appended to the cache, then
+ *     attends causally over the cached prefix and the chunk;
+ *   - one batched decode per engine tick over all active sequences, one new
+ *     token each; GQA and tanh logit softcapping (Gemma-style models).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Pointers.  Every array argument is a DEVICE pointer to caller-owned memory,
+ *   16-byte aligned, dense and row-major in the shape given.  The library
+ *   never allocates or frees memory and keeps no pointer after it returns.
+ * Streams.  `stream` is a hipStream_t (NULL = the null stream).  Calls only
+ *   enqueue work and return; buffers must stay alive until the stream has
+ *   executed it.  No call synchronises.
+ * dtype.  PKV_BF16 or PKV_F32; q, out, new K/V rows and both pools share it.
+ *   Accumulation is always fp32; bf16 results are rounded to nearest even.
+ * Block pool (vLLM/PagedAttention layout), X = 16 / sizeof(element):
+ *     k_pool [num_blocks, num_kv_heads, head_dim / X, 16, X]
+ *     v_pool [num_blocks, num_kv_heads, head_dim, 16]
+ *   Token t of sequence b lives in block block_tables[b * max_blocks_per_seq
+ *   + t / 16] at offset t % 16.  Block size is fixed at 16.
+ * Lengths.  context_lens[b] counts all cached tokens of sequence b, the token
+ *   just appended included.  A decode query sits at position
+ *   context_lens[b] - 1.
+ * GQA.  num_q_heads = gqa_group * num_kv_heads; query head h reads kv head
+ *   h / gqa_group.
+ * Window.  window > 0 keeps key t for a query at q_pos iff q_pos - t < window
+ *   (the last `window` tokens, the query's own included); <= 0 disables it.
+ * Softcap.  softcap > 0 replaces each logit s = scale * q.k by
+ *   softcap * tanh(s / softcap); <= 0 disables it.
+ * Errors.  Every `int` function returns PKV_OK (0) or a negative code; the
+ *   message of the calling thread's last failure is pkv_last_error().
+ *   Validation reads only the scalar arguments, never device memory; a failed
+ *   call enqueues nothing.  Device contents are the caller's contract
+ *   (0 <= block id < num_blocks, 0 <= context_lens[b] <=
+ *   max_blocks_per_seq * 16, distinct non-negative slots); the kernels clamp
+ *   lengths and skip out-of-range block ids and slots instead of touching
+ *   memory outside the pools, but results are then unspecified.
+ * Reentrancy.  Calls are thread-safe.  Calls that share a workspace must not
+ *   overlap in time (use one workspace per stream in flight).
+ */
+#ifndef PKV_H
+#define PKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+struct ihipStream_t; /* = hipStream_t */
+
+enum pkv_dtype { PKV_F32 = 0, PKV_BF16 = 1 };
+
+enum pkv_status {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,       /* null pointer, negative size, inconsistent shape     */
+  PKV_EUNSUPPORTED = -2, /* dtype, head_dim not in {64,128,256}, block_size != 16,
+                            gqa_group outside what the entry point supports,
+                            partition_size not a positive multiple of 16        */
+  PKV_EWORKSPACE = -3,   /* workspace null or smaller than the size query says  */
+  PKV_EHIP = -4          /* the HIP runtime reported an error at launch         */
+};
+
+#define PKV_BLOCK_SIZE 16
+
+/*
+ * paged_kv_append -- write new K/V rows into their cache slots.
+ * "Block-paged KV cache" (page "Inference Server", section "The engine"): the
+ * K/V of every new token is copied into the slot the host reserved for it;
+ * a chunk of a long prompt is appended this way before it attends (chunked
+ * prefill, page "Inference Server -- Architecture Map", section "How a single
+ * request flows through the system"), and so is each decode token.
+ *
+ *   k_new, v_new  [num_tokens, num_kv_heads, head_dim]   rows to write
+ *   slot_mapping  int32 [num_tokens]: slot = block * 16 + offset; a negative
+ *                 slot skips the token (padding).  Slots must be distinct.
+ *   k_pool, v_pool  the pools above, updated in place.
+ * The copy is bit-exact.  num_tokens == 0 is a no-op.
+ */
+int paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
+                    int32_t num_tokens, void* k_pool, void* v_pool, int32_t num_blocks,
+                    int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
+                    struct ihipStream_t* stream);
+
+/*
+ * paged_attn_decode_workspace_size -- bytes of device workspace that
+ * paged_attn_decode (partition_size == 0) or paged_attn_decode_splitk
+ * (partition_size > 0) needs for these sizes.  Depends on the arguments only.
+ * Returns 0 for invalid sizes.
+ *
+ * Workspace contract: before its FIRST use the workspace must be zero-filled
+ * (e.g. hipMemset).  Every completed call leaves its counter region zero
+ * again, so later calls need no clearing.  Contents are otherwise scratch.
+ */
+size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
+                                        int32_t gqa_group, int32_t head_dim,
+                                        int32_t max_context_len, int32_t partition_size);
+
+/*
+ * paged_attn_decode -- batched one-token decode over the block-paged cache.
+ * "Paged decode kernel reading K/V through block tables" (page "Inference
+ * Server", section "The engine"); one batched decode per tick over every
+ * active request (page "Inference Server -- Architecture Map", section "How a
+ * single request flows through the system").
+ *
+ *   out           [num_seqs, num_kv_heads * gqa_group, head_dim]
+ *   lse           optional fp32 [num_seqs, num_q_heads], natural-log
+ *                 log-sum-exp of each row's logits (NULL: not written)
+ *   q             [num_seqs, num_q_heads, head_dim]
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]
+ *   context_lens  int32 [num_seqs];  max_context_len >= every entry and
+ *                 <= max_blocks_per_seq * 16
+ *   gqa_group     1 .. 16
+ *   workspace     >= paged_attn_decode_workspace_size(..., 0) bytes
+ * The work over all (sequence, kv head, block) triples is split evenly across
+ * the GPU, partial results are merged by log-sum-exp inside the same launch.
+ * A sequence with context length 0 gets out = 0 and lse = -inf.
+ */
+int paged_attn_decode(void* out, float* lse, const void* q, const void* k_pool,
+                      const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
+                      int32_t max_blocks_per_seq, const int32_t* context_lens,
+                      int32_t max_context_len, int32_t num_seqs, int32_t num_kv_heads,
+                      int32_t gqa_group, int32_t head_dim, int32_t block_size, float scale,
+                      float softcap, int32_t window, void* workspace, size_t workspace_bytes,
+                      int32_t dtype, struct ihipStream_t* stream);
+
+/*
+ * paged_attn_decode_splitk -- the split-K decode variant (page "Inference
+ * Server", section "The engine").  Sequence b's tokens are cut into
+ * partitions [p * partition_size, (p + 1) * partition_size), anchored at
+ * token 0; each partition yields (max logit, sum of exponentials, partial
+ * output) and the partitions are merged by log-sum-exp.  Arguments as
+ * paged_attn_decode, plus
+ *   partition_size  tokens per partition, a positive multiple of 16
+ *   workspace       >= paged_attn_decode_workspace_size(..., partition_size)
+ */
+int paged_attn_decode_splitk(void* out, float* lse, const void* q, const void* k_pool,
+                             const void* v_pool, int32_t num_blocks,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t max_context_len,
+                             int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                             int32_t head_dim, int32_t block_size, float scale, float softcap,
+                             int32_t window, int32_t partition_size, void* workspace,
+                             size_t workspace_bytes, int32_t dtype, struct ihipStream_t* stream);
+
+/*
+ * paged_attn_prefill -- causal attention of a chunk of new tokens over the
+ * cached prefix plus the chunk (chunked / batched prefill, page "Inference
+ * Server", section "The engine"; "Triton paged ... prefill kernels reading
+ * K/V through block tables").  The chunk's K/V must already be in the pool
+ * (paged_kv_append); prefix blocks may be shared between sequences.
+ *
+ *   out           [num_q_tokens, num_q_heads, head_dim]
+ *   lse           optional fp32 [num_q_tokens, num_q_heads] (NULL: not written)
+ *   q             [num_q_tokens, num_q_heads, head_dim]; rows of sequence b
+ *                 are cu_q_lens[b] .. cu_q_lens[b+1]-1
+ *   cu_q_lens     int32 [num_seqs + 1], non-decreasing, cu_q_lens[0] = 0,
+ *                 cu_q_lens[num_seqs] = num_q_tokens
+ *   max_q_len     >= every n_b = cu_q_lens[b+1] - cu_q_lens[b]
+ *   context_lens  int32 [num_seqs], L_b >= n_b; query row j of sequence b
+ *                 sits at position L_b - n_b + j and sees keys t <= position
+ *   gqa_group     1, 2, 4, 8 or 16
+ */
+int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q_lens,
+                       int32_t num_q_tokens, int32_t max_q_len, const void* k_pool,
+                       const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t max_context_len, int32_t num_seqs, int32_t num_kv_heads,
+                       int32_t gqa_group, int32_t head_dim, int32_t block_size, float scale,
+                       float softcap, int32_t window, int32_t dtype, struct ihipStream_t* stream);
+
+/* Message describing the calling thread's last failed call ("" if none). */
+const char* pkv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H */

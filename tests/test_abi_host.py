@@ -1,0 +1,157 @@
+"""Host-only checks of libpkv's C ABI (no GPU needed): the library loads,
+exports every function include/pkv.h declares, sizes its workspace from the
+arguments alone, and rejects invalid scalar arguments with the documented
+error codes before any HIP call (so nothing is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_paged_kv_append_amd as pkv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkv.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(pkv.LIB_PATH),
+                                reason="libpkv.so not built (run __graft_entry__.build())")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(?:int|size_t|const char\*)\s+(\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("paged_kv_append", "paged_attn_decode", "paged_attn_decode_splitk",
+              "paged_attn_prefill", "paged_attn_decode_workspace_size", "pkv_last_error"):
+        assert n in names
+    assert set(names) == set(pkv.SIGNATURES), "binding signatures out of sync with pkv.h"
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(pkv.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+
+
+def test_header_compiles_as_c():
+    import shutil
+    import subprocess
+    import tempfile
+
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        with open(src, "w") as f:
+            f.write('#include "pkv.h"\nint main(void){return PKV_OK + PKV_BLOCK_SIZE - 16;}\n')
+        r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER),
+                            src, "-o", os.path.join(d, "t")], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_workspace_size_is_a_pure_function():
+    lib = pkv.load_library()
+    f = lib.paged_attn_decode_workspace_size
+    a = f(32, 2, 4, 256, 4096, 0)
+    assert a > 0 and a == f(32, 2, 4, 256, 4096, 0)
+    assert f(32, 2, 4, 256, 4096, 0) == f(32, 2, 4, 256, 1, 0)  # balanced split: fixed slots
+    # split-K: one slot per (sequence, kv head, partition)
+    small, big = f(8, 4, 8, 128, 32768, 512), f(8, 4, 8, 128, 32768, 256)
+    assert big > small
+    slots = 8 * 4 * 64
+    assert small >= slots * 8 * (128 + 2) * 4
+    for bad in [(-1, 2, 4, 256, 10, 0), (1, 0, 4, 256, 10, 0), (1, 2, 17, 256, 10, 0),
+                (1, 2, 4, 96, 10, 0), (1, 2, 4, 256, 10, 24), (1, 2, 4, 256, -5, 0)]:
+        assert f(*bad) == 0, bad
+
+
+def _decode_args(**over):
+    a = dict(out=16, lse=None, q=16, k_pool=16, v_pool=16, num_blocks=4, block_tables=16,
+             max_blocks_per_seq=4, context_lens=16, max_context_len=64, num_seqs=1,
+             num_kv_heads=1, gqa_group=4, head_dim=64, block_size=16, scale=0.125, softcap=0.0,
+             window=0, workspace=None, workspace_bytes=0, dtype=pkv.PKV_BF16, stream=None)
+    a.update(over)
+    return a
+
+
+def call_decode(**over):
+    a = _decode_args(**over)
+    lib = pkv.load_library()
+    return lib.paged_attn_decode(a["out"], a["lse"], a["q"], a["k_pool"], a["v_pool"],
+                                 a["num_blocks"], a["block_tables"], a["max_blocks_per_seq"],
+                                 a["context_lens"], a["max_context_len"], a["num_seqs"],
+                                 a["num_kv_heads"], a["gqa_group"], a["head_dim"],
+                                 a["block_size"], a["scale"], a["softcap"], a["window"],
+                                 a["workspace"], a["workspace_bytes"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=5), -2),
+    (dict(head_dim=96), -2),
+    (dict(block_size=32), -2),
+    (dict(gqa_group=17), -2),
+    (dict(gqa_group=0), -2),
+    (dict(num_seqs=-1), -1),
+    (dict(num_kv_heads=0), -1),
+    (dict(max_context_len=65), -1),   # > max_blocks_per_seq * 16
+    (dict(scale=float("nan")), -1),
+    (dict(q=None), -1),
+    (dict(out=24), -1),               # not 16-byte aligned
+    (dict(), -3),                     # no workspace
+    (dict(workspace=256, workspace_bytes=16), -3),
+])
+def test_decode_rejects_bad_arguments(over, code):
+    assert call_decode(**over) == code
+    assert pkv.pkv_last_error().startswith("paged_attn_decode")
+
+
+def test_empty_batch_is_a_no_op():
+    assert call_decode(num_seqs=0, out=None, q=None) == 0
+
+
+def test_splitk_rejects_bad_partition():
+    lib = pkv.load_library()
+    a = _decode_args()
+    for P in (0, 24, -16):
+        rc = lib.paged_attn_decode_splitk(a["out"], None, a["q"], a["k_pool"], a["v_pool"], 4, 16,
+                                          4, 16, 64, 1, 1, 4, 64, 16, 0.125, 0.0, 0, P, None, 0,
+                                          pkv.PKV_BF16, None)
+        assert rc == -2
+        assert "partition_size" in pkv.pkv_last_error()
+
+
+def test_append_rejects_bad_arguments():
+    lib = pkv.load_library()
+    ok = dict(k=16, v=16, s=16, T=4, kp=16, vp=16, nb=2, hkv=1, d=64, bs=16, dt=pkv.PKV_BF16)
+
+    def call(**o):
+        a = dict(ok, **o)
+        return lib.paged_kv_append(a["k"], a["v"], a["s"], a["T"], a["kp"], a["vp"], a["nb"],
+                                   a["hkv"], a["d"], a["bs"], a["dt"], None)
+
+    assert call(T=-1) == -1
+    assert call(dt=9) == -2
+    assert call(d=100) == -2
+    assert call(bs=8) == -2
+    assert call(k=None) == -1
+    assert call(nb=0) == -1
+    assert call(T=0, k=None, v=None, s=None) == 0  # nothing to do
+
+
+def test_prefill_rejects_bad_arguments():
+    lib = pkv.load_library()
+
+    def call(G=4, Tq=8, mq=8, mctx=64, cu=16):
+        return lib.paged_attn_prefill(16, None, 16, cu, Tq, mq, 16, 16, 4, 16, 4, 16, mctx, 1, 1, G,
+                                      64, 16, 0.125, 0.0, 0, pkv.PKV_BF16, None)
+
+    assert call(G=3) == -2        # must divide 16
+    assert call(mq=65) == -1      # longer than any context
+    assert call(cu=None) == -1
+    assert call(Tq=-1) == -1

@@ -1,0 +1,258 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle on
+identical seeded inputs.
+
+* append: bit-exact on the whole pools, NaN poison included;
+* attention: every output element within |gpu - ref| <= 2e-2 + 1e-2 |ref|
+  for bf16 (1e-4 + 1e-4 |ref| for fp32), a relative-RMS gate, no NaN, and the
+  log-sum-exp within 2e-3.
+
+Small cases span several tiles and ragged tails; the named workloads run at
+their full sizes in the launch configuration the benchmark times.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_paged_kv_append_amd as pkv
+import oracle
+from block_paged_kv_append_amd import workloads as wl
+from tests.gpu_common import (check_close, check_lse, dev, i32, oracle_decode, run_append,
+                              run_decode, run_prefill)
+
+pytestmark = pytest.mark.gpu
+
+
+def banner(*what):
+    print("\n[case]", *what, flush=True)
+
+
+# ---------------------------------------------------------------------------
+# append
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("D", [64, 128, 256])
+def test_append_bit_exact(dtype, D):
+    case = wl.make_prefill_case(200 + D, [5, 16, 31, 0], [11, 17, 2, 40], 4, 2, D, dtype)
+    slots = case.slot_mapping.copy()
+    slots[[3, 20]] = -1  # padding tokens
+    case.slot_mapping = slots
+    banner("append", dtype, D)
+    kp, vp = run_append(case)
+    kr, vr = oracle.append(case.k_new, case.v_new, slots, case.k_pool, case.v_pool, dtype)
+    assert np.array_equal(pkv.to_bits(kp).reshape(kr.shape), kr)
+    assert np.array_equal(pkv.to_bits(vp).reshape(vr.shape), vr)
+
+
+def test_append_single_token_per_sequence():
+    """The decode-time append: one new token for each of many sequences."""
+    case = wl.make_prefill_case(210, list(range(3, 3 + 40 * 7, 7)), [1] * 40, 8, 2, 256, "bf16")
+    banner("append decode-style")
+    kp, vp = run_append(case)
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           "bf16")
+    assert np.array_equal(pkv.to_bits(kp), kr) and np.array_equal(pkv.to_bits(vp), vr)
+
+
+def test_append_full_chunked_prefill_workload():
+    case = wl.chunked_prefill_shared_prefix()
+    banner("append full", case.name)
+    kp, vp = run_append(case)
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           case.dtype)
+    assert np.array_equal(pkv.to_bits(kp), kr) and np.array_equal(pkv.to_bits(vp), vr)
+
+
+# ---------------------------------------------------------------------------
+# decode (balanced split) and split-K decode on small ragged cases
+# ---------------------------------------------------------------------------
+SMALL_DECODE = [
+    # (lens, Hq, Hkv, D, dtype, softcap, window)
+    ([1, 15, 16, 17, 33, 100], 4, 1, 64, "bf16", 0.0, 0),
+    ([1, 15, 16, 17, 33, 100], 4, 1, 64, "f32", 0.0, 0),
+    ([7, 300, 64, 1000, 129], 8, 2, 128, "bf16", 5.0, 0),
+    ([7, 300, 64, 1000, 129], 8, 2, 256, "bf16", 0.0, 100),
+    ([250, 31, 1, 513], 16, 16, 128, "bf16", 0.0, 17),
+    ([250, 31, 1, 513], 3, 1, 64, "bf16", 2.0, 0),     # group 3: padded head columns
+    ([2000, 12, 700], 16, 1, 256, "bf16", 30.0, 0),    # group 16
+    ([40, 17], 2, 1, 128, "f32", 1.5, 16),
+    ([4096] * 3 + [17], 8, 2, 256, "bf16", 50.0, 512),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL_DECODE, ids=lambda s: f"L{len(s[0])}-G{s[1]//s[2]}-D{s[3]}-{s[4]}-c{s[5]}-w{s[6]}")
+@pytest.mark.parametrize("mode", ["balanced", "splitk16", "splitk64", "splitk512"])
+def test_decode_small(spec, mode):
+    lens, Hq, Hkv, D, dtype, cap, W = spec
+    case = wl.make_decode_case(300 + sum(lens) % 97, lens, Hq, Hkv, D, dtype, softcap=cap, window=W)
+    banner("decode", mode, spec)
+    if mode == "balanced":
+        out, lse = run_decode(case)
+    else:
+        out, lse = run_decode(case, "splitk", int(mode[6:]))
+    ref, ref_lse = oracle_decode(case)
+    check_close(out, ref, dtype, f"decode {mode}")
+    check_lse(lse, ref_lse, f"decode {mode}")
+
+
+def test_decode_empty_sequences():
+    case = wl.make_decode_case(311, [0, 40, 0, 17], 4, 2, 64, "bf16")
+    for mode, P in (("balanced", None), ("splitk", 32)):
+        banner("decode empty", mode)
+        out, lse = run_decode(case, mode, P)
+        ref, ref_lse = oracle_decode(case)
+        assert (out[0] == 0).all() and (out[2] == 0).all()
+        check_close(out, ref, "bf16", mode)
+        check_lse(lse, ref_lse, mode)
+
+
+def test_decode_workspace_reused_across_calls():
+    """Counters must be left at zero: two calls in a row on one workspace,
+    the second with a smaller batch, both correct."""
+    big = wl.make_decode_case(321, [3000, 17, 900, 2048, 5], 8, 2, 128, "bf16", softcap=20.0)
+    small = wl.make_decode_case(322, [100, 1500], 8, 2, 128, "bf16")
+    need = max(pkv.paged_attn_decode_workspace_size(5, 2, 4, 128, 3000, 0),
+               pkv.paged_attn_decode_workspace_size(5, 2, 4, 128, 3000, 64))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for mode, P in (("balanced", None), ("splitk", 64)):
+        for case in (big, small, big):
+            banner("decode reuse", mode, case.context_lens.tolist())
+            out, lse = run_decode(case, mode, P, workspace=ws)
+            ref, ref_lse = oracle_decode(case)
+            check_close(out, ref, "bf16", mode)
+            check_lse(lse, ref_lse, mode)
+
+
+def test_decode_without_lse_output():
+    case = wl.make_decode_case(331, [77, 1200], 8, 2, 256, "bf16")
+    banner("decode no-lse")
+    out, _ = run_decode(case, with_lse=False)
+    check_close(out, oracle_decode(case)[0], "bf16", "no lse")
+
+
+def test_decode_poisoned_table_padding_is_never_read():
+    """Table entries past each sequence point at NaN blocks; lengths that end
+    exactly on a block boundary must not read the next entry."""
+    case = wl.make_decode_case(341, [16, 32, 48, 160], 4, 1, 128, "bf16", max_blocks_per_seq=16)
+    banner("decode block-boundary")
+    out, lse = run_decode(case)
+    check_close(out, oracle_decode(case)[0], "bf16", "boundary")
+
+
+# ---------------------------------------------------------------------------
+# the named workloads at full size
+# ---------------------------------------------------------------------------
+def test_tiny_decode_fp32():
+    case = wl.tiny_decode_fp32()
+    for mode, P in (("balanced", None), ("splitk", 16)):
+        banner(case.name, mode)
+        out, lse = run_decode(case, mode, P)
+        ref, ref_lse = oracle_decode(case)
+        check_close(out, ref, "f32", mode)
+        check_lse(lse, ref_lse, mode)
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 8.0, 40.0], ids=["plain", "peaked", "softcap-stress"])
+def test_gemma_decode_full(q_scale):
+    case = wl.gemma_decode(q_scale=q_scale)
+    banner(case.name, q_scale)
+    out, lse = run_decode(case)
+    ref, ref_lse = oracle_decode(case)
+    check_close(out, ref, "bf16", case.name)
+    check_lse(lse, ref_lse, case.name)
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 8.0], ids=["plain", "peaked"])
+def test_sliding_window_decode_full(q_scale):
+    case = wl.sliding_window_decode(q_scale=q_scale)
+    banner(case.name, q_scale)
+    out, lse = run_decode(case)
+    ref, ref_lse = oracle_decode(case)
+    check_close(out, ref, "bf16", case.name)
+    check_lse(lse, ref_lse, case.name)
+
+
+@pytest.mark.parametrize("mode", ["splitk", "balanced"])
+def test_long_context_splitk_full(mode):
+    case = wl.long_context_splitk(q_scale=8.0)
+    banner(case.name, mode)
+    out, lse = run_decode(case, mode)
+    ref, ref_lse = oracle_decode(case)
+    check_close(out, ref, "bf16", case.name)
+    check_lse(lse, ref_lse, case.name)
+
+
+def test_long_context_plain_inputs_sampled():
+    """Unscaled q: the softmax is nearly flat over 32768 keys; compare every
+    output and also the per-partition split-K algebra against the oracle's."""
+    case = wl.long_context_splitk()
+    banner(case.name, "plain")
+    out, lse = run_decode(case, "splitk")
+    ref, ref_lse = oracle_decode(case)
+    check_close(out, ref, "bf16", case.name)
+    check_lse(lse, ref_lse, case.name)
+
+
+# ---------------------------------------------------------------------------
+# prefill
+# ---------------------------------------------------------------------------
+SMALL_PREFILL = [
+    # (cached, chunk, Hq, Hkv, D, dtype, softcap, window, shared_blocks)
+    ([0, 16, 33], [40, 16, 5], 4, 1, 64, "bf16", 0.0, 0, 0),
+    ([0, 16, 33], [40, 16, 5], 4, 1, 64, "f32", 0.0, 0, 0),
+    ([64, 80, 100], [70, 1, 129], 8, 2, 128, "bf16", 10.0, 0, 4),
+    ([300, 1], [200, 90], 8, 1, 256, "bf16", 0.0, 64, 0),
+    ([48, 48], [77, 3], 2, 2, 128, "bf16", 0.0, 0, 3),      # group 1
+    ([20, 5], [33, 64], 16, 1, 64, "bf16", 3.0, 0, 0),      # group 16
+    ([20, 5], [33, 64], 16, 8, 128, "bf16", 0.0, 19, 0),    # group 2
+    ([513], [250], 8, 2, 256, "f32", 0.0, 0, 0),
+]
+
+
+@pytest.mark.parametrize("spec", SMALL_PREFILL,
+                         ids=lambda s: f"G{s[2]//s[3]}-D{s[4]}-{s[5]}-c{s[6]}-w{s[7]}-s{s[8]}")
+def test_prefill_small(spec):
+    cached, chunk, Hq, Hkv, D, dtype, cap, W, shared = spec
+    case = wl.make_prefill_case(400 + D + sum(chunk), cached, chunk, Hq, Hkv, D, dtype,
+                                softcap=cap, window=W, shared_prefix_blocks=shared)
+    banner("prefill", spec)
+    kp, vp = run_append(case)
+    out, lse = run_prefill(case, kp, vp)
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           dtype)
+    ref, ref_lse = oracle.prefill(case.q, case.cu_q_lens, kr, vr, case.block_tables,
+                                  case.context_lens, case.scale, case.softcap, case.window, dtype)
+    check_close(out, ref, dtype, "prefill")
+    check_lse(lse, ref_lse, "prefill")
+
+
+@pytest.mark.parametrize("q_scale", [1.0, 8.0], ids=["plain", "peaked"])
+def test_chunked_prefill_full(q_scale):
+    case = wl.chunked_prefill_shared_prefix(q_scale=q_scale)
+    banner(case.name, q_scale)
+    kp, vp = run_append(case)
+    out, lse = run_prefill(case, kp, vp)
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           case.dtype)
+    assert np.array_equal(pkv.to_bits(kp), kr) and np.array_equal(pkv.to_bits(vp), vr)
+    ref, ref_lse = oracle.prefill(case.q, case.cu_q_lens, kr, vr, case.block_tables,
+                                  case.context_lens, case.scale, case.softcap, case.window,
+                                  case.dtype)
+    check_close(out, ref, "bf16", case.name)
+    check_lse(lse, ref_lse, case.name)
+
+
+def test_prefill_single_row_equals_decode():
+    """A one-token chunk is a decode step: both entry points agree."""
+    case = wl.make_prefill_case(451, [100, 700, 31], [1, 1, 1], 8, 2, 256, "bf16", softcap=50.0)
+    banner("prefill n=1 vs decode")
+    kp, vp = run_append(case)
+    out, _ = run_prefill(case, kp, vp)
+    q = dev(case.q, "bf16")
+    dout = torch.empty_like(q)
+    pkv.paged_attn_decode(dout, q, kp, vp, i32(case.block_tables), i32(case.context_lens),
+                          case.max_context_len, case.scale, case.softcap, 0)
+    torch.cuda.synchronize()
+    d = np.abs(out - dout.float().cpu().numpy())
+    assert d.max() <= 2e-2
