@@ -27,6 +27,18 @@
 
 namespace pkv {
 
+// Wait states between a matrix-core result and its first reader.  The
+// compiler's hazard padding does not always reach a read that follows the
+// last matrix op across a branch (seen on gfx950: an accumulator read two
+// instructions after a 16x16x32 product on a taken-branch path); 24 wait
+// states cover the longest (16-pass) products.  The scheduling barriers keep
+// the products before and every reader after the padding.
+__device__ __forceinline__ void mma_result_fence() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 template <bool BF16>
 struct Elem;
 template <>
@@ -101,6 +113,7 @@ __device__ __forceinline__ f32x4 qk_tile(const KVFrag<true, D>& f, const QFrag<t
     s0 = mma_bf16_k32(f.k[i], q.q[i], s0);
     if (i + 1 < KVFrag<true, D>::KS) s1 = mma_bf16_k32(f.k[i + 1], q.q[i + 1], s1);
   }
+  mma_result_fence();
   return s0 + s1;
 }
 
@@ -173,6 +186,7 @@ __device__ __forceinline__ f32x4 qk_tile(const KVFrag<false, D>& f, const QFrag<
     s = mma_f32_k4(f.k[i].z, q.q[i].z, s);
     s = mma_f32_k4(f.k[i].w, q.q[i].w, s);
   }
+  mma_result_fence();
   return s;
 }
 

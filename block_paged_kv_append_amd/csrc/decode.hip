@@ -153,7 +153,7 @@ __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = tok0 + 4 * j + r;
-      const bool vis = ok && t >= sp.vis_lo && t < sp.L;
+      const bool vis = ok & (t >= sp.vis_lo) & (t < sp.L);
       s2[r] = vis ? xf(sc[r]) : kNegInf;
     }
     float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
@@ -200,6 +200,7 @@ __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece
   }
 
   // ---- combine the four waves through LDS ----
+  mma_result_fence();
   float l_tot = l_run + __shfl_xor(l_run, 16);
   l_tot += __shfl_xor(l_tot, 32);
   float* lo = lds;                      // [4][G][D]

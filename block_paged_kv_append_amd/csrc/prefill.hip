@@ -108,8 +108,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int tk = tok0 + 4 * j + r;
-        bool vis = ok && rvalid[t] && tk < L && tk <= qpos[t];
-        if (a.window > 0) vis = vis && (qpos[t] - tk < a.window);
+        const bool vis = ok & rvalid[t] & (tk < L) & (tk <= qpos[t]) &
+                         ((a.window <= 0) | (qpos[t] - tk < a.window));
         s2[r] = vis ? xf(sc[r]) : kNegInf;
       }
       float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
@@ -152,6 +152,7 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   }
 
   // ---- finalize: rows 4j + r of each tile ----
+  mma_result_fence();
 #pragma unroll
   for (int t = 0; t < RT; ++t) {
     float l_tot = l_run[t] + __shfl_xor(l_run[t], 16);
@@ -187,21 +188,22 @@ hipError_t launch_p(PrefillArgs a, hipStream_t stream) {
 
 }  // namespace
 
-int prefill_row_tiles(int head_dim) { return head_dim >= 256 ? 2 : 4; }
+// Row tiles per wave: two at head_dim 64/128, one at 256 (register budget).
+int prefill_row_tiles(int head_dim) { return head_dim >= 256 ? 1 : 2; }
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, hipStream_t stream) {
   if (a.num_items <= 0) return hipSuccess;
   if (bf16) {
     switch (head_dim) {
-      case 64: return launch_p<true, 64, 4>(a, stream);
-      case 128: return launch_p<true, 128, 4>(a, stream);
-      case 256: return launch_p<true, 256, 2>(a, stream);
+      case 64: return launch_p<true, 64, 2>(a, stream);
+      case 128: return launch_p<true, 128, 2>(a, stream);
+      case 256: return launch_p<true, 256, 1>(a, stream);
     }
   } else {
     switch (head_dim) {
-      case 64: return launch_p<false, 64, 4>(a, stream);
-      case 128: return launch_p<false, 128, 4>(a, stream);
-      case 256: return launch_p<false, 256, 2>(a, stream);
+      case 64: return launch_p<false, 64, 2>(a, stream);
+      case 128: return launch_p<false, 128, 2>(a, stream);
+      case 256: return launch_p<false, 256, 1>(a, stream);
     }
   }
   return hipErrorInvalidValue;
