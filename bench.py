@@ -9,7 +9,8 @@ is algorithmic HBM bytes per second of the whole step (K/V read once per kv
 head, q read, output written, table entries and lengths, the appended rows
 read and written).  The pool is replicated R times in HBM and consecutive
 steps read different replicas, so that no step is served from the 256 MB
-Infinity Cache by its predecessor.
+Infinity Cache by its predecessor.  Each step is captured once per replica as
+a HIP graph and replayed, as an engine replays its captured decode step.
 
 Also reported on the same line: the decode kernel's roofline (HIP-event
 timing of the decode launches inside the timed region), the chunked-prefill
@@ -162,30 +163,67 @@ class DecodeBench:
         self.pkv.paged_kv_append(self.k_new, self.v_new, self.slots[r], self.kp, self.vp)
 
 
+def capture(torch, fn):
+    """A HIP graph of whatever ``fn`` launches on the current stream."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    return g
+
+
 def time_steps(bench, steps, warmup, with_append, torch):
-    for i in range(warmup):
-        if with_append:
-            bench.append(i % bench.R)
-        bench.decode(i % bench.R)
+    """One HIP graph holds R consecutive steps, one per pool replica (as an
+    engine's captured decode step holds every layer's attention); each step
+    appends the tick's new rows, then decodes.  Returns the wall time of
+    ``steps`` steps (``steps / R`` replays, rounded up to whole replays)."""
+    def all_steps():
+        for r in range(bench.R):
+            if with_append:
+                bench.append(r)
+            bench.decode(r)
+
+    all_steps()  # eager warm-up
     torch.cuda.synchronize()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(steps)]
+    g = capture(torch, all_steps)
+    reps = max(1, -(-steps // bench.R))
+    for _ in range(max(1, -(-warmup // bench.R))):
+        g.replay()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(steps):
-        r = (warmup + i) % bench.R
-        if with_append:
-            bench.append(r)
+    for _ in range(reps):
+        g.replay()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * steps / (reps * bench.R)
+
+
+def time_decode_op(bench, iters, torch):
+    """Average duration of one decode operation: a graph of R decode calls
+    (one per replica) replayed ``iters`` times, each replay bracketed by HIP
+    events on the stream, divided by R."""
+    import numpy as np
+
+    def all_decodes():
+        for r in range(bench.R):
+            bench.decode(r)
+
+    all_decodes()
+    torch.cuda.synchronize()
+    g = capture(torch, all_decodes)
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for i in range(iters):
         ev[i][0].record()
-        bench.decode(r)
+        g.replay()
         ev[i][1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    return wall, kern_ms
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) / bench.R
 
 
 def time_prefill(case, iters, warmup, torch, pkv):
+    """Average durations of the chunk append and of the prefill, each replayed
+    from its own graph and bracketed by HIP events."""
     import numpy as np
 
     dt = case.dtype
@@ -206,22 +244,24 @@ def time_prefill(case, iters, warmup, torch, pkv):
         pkv.paged_attn_prefill(out, q, cu, case.max_q_len, kp, vp, bt, cl, case.max_context_len,
                                case.scale, case.softcap, case.window)
 
-    for _ in range(warmup):
-        append()
-        prefill()
+    append()
+    prefill()
     torch.cuda.synchronize()
-    ea = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-    ep = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
-    for i in range(iters):
-        ea[i][0].record()
-        append()
-        ea[i][1].record()
-        ep[i][0].record()
-        prefill()
-        ep[i][1].record()
-    torch.cuda.synchronize()
-    return (float(np.mean([a.elapsed_time(b) for a, b in ea])),
-            float(np.mean([a.elapsed_time(b) for a, b in ep])))
+    ga, gp = capture(torch, append), capture(torch, prefill)
+    res = []
+    for g in (ga, gp):
+        for _ in range(warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for i in range(iters):
+            ev[i][0].record()
+            g.replay()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        res.append(float(np.mean([a.elapsed_time(b) for a, b in ev])))
+    return res[0], res[1]
 
 
 def calibrate_copy(torch):
@@ -293,12 +333,12 @@ def main():
     print(f"# setup {time.perf_counter() - t_setup:.1f}s, pool replicas {bench.R}", file=sys.stderr,
           flush=True)
 
-    wall, kern_ms = time_steps(bench, args.steps, args.warmup, True, torch)
+    wall = time_steps(bench, args.steps, args.warmup, True, torch)
     ms_per_step = wall * 1e3 / args.steps
     dbytes = decode_bytes(case)
     abytes = append_bytes(case.num_seqs, case.num_kv_heads, case.head_dim, 2)
     value = (dbytes + abytes) / (ms_per_step * 1e-3) / 1e9
-    kern_avg_ms = float(np.mean(kern_ms))
+    kern_avg_ms = time_decode_op(bench, max(10, args.steps // bench.R), torch)
     achieved = dbytes / (kern_avg_ms * 1e-3) / 1e9
     traffic = measured_traffic("decode")
     line = {
@@ -322,7 +362,8 @@ def main():
         "hbm_frac_step": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel": "decode_kernel (balanced split)",
+                     "traffic": traffic,
+                     "kernel": "paged_attn_decode: decode_kernel (balanced split) + merge_kernel",
                      "kernel_ms": round(kern_avg_ms, 5), "algorithmic_bytes": dbytes},
     }
 
@@ -347,8 +388,7 @@ def main():
         for maker in (wl.sliding_window_decode, wl.long_context_splitk):
             c = maker()
             b = DecodeBench(c, 0, torch, pkv)
-            _, km = time_steps(b, 50, 5, False, torch)
-            ms = float(np.mean(km))
+            ms = time_decode_op(b, 20, torch)
             gbs = decode_bytes(c) / (ms * 1e-3) / 1e9
             extra[c.name] = {"ms": round(ms, 5), "gbs": round(gbs, 1),
                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),

@@ -12,14 +12,6 @@
 
 #include "launch.hpp"
 
-// Tuning of the balanced decode split (compile-time; see the decode kernel).
-#ifndef PKV_DECODE_WGS_PER_CU
-#define PKV_DECODE_WGS_PER_CU 2
-#endif
-#ifndef PKV_DECODE_MIN_BLOCKS_PER_WG
-#define PKV_DECODE_MIN_BLOCKS_PER_WG 8
-#endif
-
 namespace {
 
 thread_local char g_err[512] = "";
@@ -156,8 +148,6 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
   const size_t slots =
       pkv::decode_num_slots(num_seqs, num_kv_heads, max_context_len, partition_size);
   char* base = static_cast<char*>(workspace);
-  a.counters = reinterpret_cast<int32_t*>(base);
-  base += align256((size_t)num_seqs * num_kv_heads * sizeof(int32_t));
   a.part_o = reinterpret_cast<float*>(base);
   base += align256(slots * gqa_group * head_dim * sizeof(float));
   a.part_ml = reinterpret_cast<float*>(base);
@@ -173,16 +163,11 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
     int cus = 0;
     rc = cu_count(&cus);
     if (rc != PKV_OK) return rc;
-    const long long units = (long long)num_seqs * num_kv_heads *
-                            max_units_per_seq(max_context_len, window);
-    long long n = (units + PKV_DECODE_MIN_BLOCKS_PER_WG - 1) / PKV_DECODE_MIN_BLOCKS_PER_WG;
-    const long long cap = (long long)cus * PKV_DECODE_WGS_PER_CU;
-    if (n > cap) n = cap;
-    if (n > pkv::kMaxWorkers) n = pkv::kMaxWorkers;
-    if (n < 1) n = 1;
+    a.cu_count = cus;
+    a.units_bound = (long long)num_seqs * num_kv_heads * max_units_per_seq(max_context_len, window);
     a.part_blocks = 0;
     a.num_partitions = 0;
-    a.num_workers = (int32_t)n;
+    a.num_workers = 0;  // chosen by launch_decode for the kernel variant
   }
   return from_hip(pkv::launch_decode(a, head_dim, dtype == PKV_BF16, stream), fn);
 }
@@ -201,8 +186,7 @@ size_t decode_num_slots(int32_t num_seqs, int32_t num_kv_heads, int32_t max_cont
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
                               int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
   const size_t slots = decode_num_slots(num_seqs, num_kv_heads, max_context_len, partition_size);
-  return align256((size_t)num_seqs * num_kv_heads * sizeof(int32_t)) +
-         align256(slots * gqa_group * head_dim * sizeof(float)) +
+  return align256(slots * gqa_group * head_dim * sizeof(float)) +
          align256(slots * gqa_group * 2 * sizeof(float));
 }
 

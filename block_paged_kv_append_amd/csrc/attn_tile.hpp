@@ -63,19 +63,28 @@ struct KVFrag<true, D> {
   u32x4 k[KS];
   u32x2 v[NT];
 
-  __device__ __forceinline__ void load(const uint16_t* kt, const uint16_t* vt, int lane) {
-    const int c = lane & 15, j = lane >> 4;
+  __device__ __forceinline__ void load_k(const uint16_t* kt, int lane) {
 #pragma unroll
     for (int i = 0; i < KS; ++i) k[i] = *reinterpret_cast<const u32x4*>(kt + (i * kWave + lane) * 8);
+  }
+  __device__ __forceinline__ void load_v(const uint16_t* vt, int lane) {
+    const int c = lane & 15, j = lane >> 4;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       v[t] = *reinterpret_cast<const u32x2*>(vt + (t * 16 + c) * kBlock + 4 * j);
   }
+  __device__ __forceinline__ void load(const uint16_t* kt, const uint16_t* vt, int lane) {
+    load_k(kt, lane);
+    load_v(vt, lane);
+  }
+  __device__ __forceinline__ void zero_v() {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[t] = u32x2{0, 0};
+  }
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < KS; ++i) k[i] = u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int t = 0; t < NT; ++t) v[t] = u32x2{0, 0};
+    zero_v();
   }
   // Zero the V entries of tokens 4j + r >= n_valid (tail slots of a block may
   // hold anything, NaN included; a zero weight times NaN would still be NaN).
@@ -134,19 +143,28 @@ struct KVFrag<false, D> {
   f32x4 k[KS];
   f32x4 v[NT];
 
-  __device__ __forceinline__ void load(const float* kt, const float* vt, int lane) {
-    const int c = lane & 15, j = lane >> 4;
+  __device__ __forceinline__ void load_k(const float* kt, int lane) {
 #pragma unroll
     for (int i = 0; i < KS; ++i) k[i] = *reinterpret_cast<const f32x4*>(kt + (i * kWave + lane) * 4);
+  }
+  __device__ __forceinline__ void load_v(const float* vt, int lane) {
+    const int c = lane & 15, j = lane >> 4;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
       v[t] = *reinterpret_cast<const f32x4*>(vt + (t * 16 + c) * kBlock + 4 * j);
   }
+  __device__ __forceinline__ void load(const float* kt, const float* vt, int lane) {
+    load_k(kt, lane);
+    load_v(vt, lane);
+  }
+  __device__ __forceinline__ void zero_v() {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   __device__ __forceinline__ void zero() {
 #pragma unroll
     for (int i = 0; i < KS; ++i) k[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < NT; ++t) v[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    zero_v();
   }
   __device__ __forceinline__ void mask_v_tail(int n_valid, int lane) {
     const int t0 = 4 * (lane >> 4);
@@ -202,6 +220,68 @@ __device__ __forceinline__ void pv_tile(f32x4 (&o)[D / 16], const float (&p)[4],
     o[t] = mma_f32_k4(p[3], f.v[t].w, o[t]);
   }
 }
+
+// Walk blocks 0 .. cnt-1 (cnt >= 1): fetch(buf, i) issues block i's loads and
+// returns whether it is valid, step(buf, ok, i) consumes it.  With PREFETCH,
+// block i + 1 is in flight while block i is computed (two register buffers);
+// the steady-state loop always prefetches and the last one or two blocks are
+// peeled off, so every path has the same loads outstanding and the compiler's
+// wait counts stay exact.
+template <bool PREFETCH, typename KV, typename Fetch, typename Step>
+__device__ __forceinline__ void walk_blocks(int cnt, Fetch&& fetch, Step&& step) {
+  if constexpr (PREFETCH) {
+    KV bufA, bufB;
+    bool okA = fetch(bufA, 0), okB;
+    int i = 0;
+    for (; i + 2 < cnt; i += 2) {
+      okB = fetch(bufB, i + 1);
+      step(bufA, okA, i);
+      okA = fetch(bufA, i + 2);
+      step(bufB, okB, i + 1);
+    }
+    if (i + 1 < cnt) {
+      okB = fetch(bufB, i + 1);
+      step(bufA, okA, i);
+      step(bufB, okB, i + 1);
+    } else {
+      step(bufA, okA, i);
+    }
+  } else {
+    for (int i = 0; i < cnt; ++i) {
+      KV buf;
+      const bool ok = fetch(buf, i);
+      step(buf, ok, i);
+    }
+  }
+}
+
+// Walk blocks 0 .. cnt-1 (cnt >= 1) through a ring of NBUF register buffers:
+// the loads of block i + NBUF - 1 are issued before block i is computed, so
+// NBUF - 1 blocks stay in flight.  Loads are unconditional (past the end they
+// re-read the last block, an L2 hit) so the compiler's wait counts stay exact;
+// compute steps past the end are skipped.  Each refill waits out the wait
+// states of the matrix ops that read the buffer last.
+template <int NBUF, typename Buf, typename Fetch, typename Step>
+__device__ __forceinline__ void walk_ring(int cnt, Fetch&& fetch, Step&& step) {
+  Buf buf[NBUF];
+  bool ok[NBUF];
+#pragma unroll
+  for (int u = 0; u < NBUF - 1; ++u) ok[u] = fetch(buf[u], min(u, cnt - 1));
+  for (int i = 0; i < cnt; i += NBUF) {
+#pragma unroll
+    for (int u = 0; u < NBUF; ++u) {
+      const int nb = (u + NBUF - 1) % NBUF;
+      mma_result_fence();
+      ok[nb] = fetch(buf[nb], min(i + u + NBUF - 1, cnt - 1));
+      if (i + u < cnt) step(buf[u], ok[u], i + u);
+    }
+  }
+}
+
+// Double-buffer unless two fragments would not fit the register file (fp32
+// at head_dim 256: 128 registers per block).
+template <bool BF16, int D>
+constexpr bool kPrefetch = BF16 || D <= 128;
 
 // Store 4 consecutive output elements.
 __device__ __forceinline__ void store4(uint16_t* dst, f32x4 v) {

@@ -39,11 +39,12 @@ struct DecodeArgs {
   float scale;
   float softcap;  // <= 0: off
   // workspace views
-  int32_t* counters;  // [num_seqs * num_kv_heads], zero between calls
   float* part_o;      // [num_slots, gqa_group, head_dim]
   float* part_ml;     // [num_slots, gqa_group, 2]  (max logit in log2 units, sum of 2^(s-m))
   // work decomposition
-  int32_t num_workers;      // grid size
+  int32_t cu_count;         // compute units of the device
+  long long units_bound;    // upper bound on (sequence, kv head, block) units
+  int32_t num_workers;      // grid size (set by launch_decode in balanced mode)
   int32_t part_blocks;      // 0: balanced split of all blocks; > 0: fixed partitions of this many blocks
   int32_t num_partitions;   // fixed partitions per sequence
 };
@@ -70,8 +71,8 @@ struct PrefillArgs {
   int32_t num_items;      // grid size
 };
 
-// Decode workspace geometry: counters first (256-byte aligned), then the
-// partial outputs, then the (max, sum) pairs.
+// Decode workspace geometry: the partial outputs, then their (max, sum)
+// pairs, each 256-byte aligned.
 constexpr int kMaxWorkers = 1024;  // balanced split: at most this many workgroups
 size_t decode_num_slots(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                         int32_t partition_size);

@@ -29,7 +29,9 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   using T = typename Elem<BF16>::T;
   using KV = KVFrag<BF16, D>;
   constexpr int NT = D / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  // wave index as a uniform (scalar) value: table lookups become scalar loads
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, j = lane >> 4;
   const int G = a.gqa_group, Hkv = a.num_kv_heads, Hq = G * Hkv;
   const int PP = 16 / G;  // positions per row tile
@@ -87,20 +89,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   const T* vpool = reinterpret_cast<const T*>(a.v_pool);
   constexpr size_t kTile = (size_t)D * kBlock;
 
+  // Table entries of blocks blk_lo .. blk_hi, 64 at a time, one per lane;
+  // loads are unconditional (an out-of-range entry reads block 0 and is masked
+  // out) so that every path keeps the same loads in flight.
+  int tbl = 0, tbl_base = blk_lo;
   auto fetch = [&](KV& buf, int blk) -> bool {
-    const int phys = bt[blk];
-    if ((unsigned)phys >= (unsigned)a.num_blocks) {
-      buf.zero();
-      return false;
-    }
-    const size_t off = ((size_t)phys * Hkv + g) * kTile;
+    const int phys = __builtin_amdgcn_readlane(tbl, (blk - tbl_base) & 63);
+    const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
+    const size_t off = ((size_t)(ok ? phys : 0) * Hkv + g) * kTile;
     buf.load(kpool + off, vpool + off, lane);
-    return true;
+    return ok;
   };
 
   auto step = [&](KV& buf, bool ok, int blk) {
     const int tok0 = blk * kBlock;
-    if (ok && tok0 + kBlock > L) buf.mask_v_tail(L - tok0, lane);
+    if (!ok)
+      buf.zero();
+    else if (tok0 + kBlock > L)
+      buf.mask_v_tail(L - tok0, lane);
 #pragma unroll
     for (int t = 0; t < RT; ++t) {
       const f32x4 sc = qk_tile<D>(buf, qf[t]);
@@ -137,18 +143,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  KV bufA, bufB;
-  bool okA = false, okB = false;
-  int blk = blk_lo;
-  okA = fetch(bufA, blk);
-  while (blk <= blk_hi) {
-    if (blk + 1 <= blk_hi) okB = fetch(bufB, blk + 1);
-    step(bufA, okA, blk);
-    ++blk;
-    if (blk > blk_hi) break;
-    if (blk + 1 <= blk_hi) okA = fetch(bufA, blk + 1);
-    step(bufB, okB, blk);
-    ++blk;
+  for (tbl_base = blk_lo; tbl_base <= blk_hi; tbl_base += 64) {
+    const int cnt = min(64, blk_hi - tbl_base + 1);
+    tbl = lane < cnt ? bt[tbl_base + lane] : 0;
+    walk_blocks<kPrefetch<BF16, D>, KV>(
+        cnt, [&](KV& buf, int i) { return fetch(buf, tbl_base + i); },
+        [&](KV& buf, bool ok, int i) { step(buf, ok, tbl_base + i); });
   }
 
   // ---- finalize: rows 4j + r of each tile ----

@@ -102,9 +102,8 @@ int paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot_ma
  * (partition_size > 0) needs for these sizes.  Depends on the arguments only.
  * Returns 0 for invalid sizes.
  *
- * Workspace contract: before its FIRST use the workspace must be zero-filled
- * (e.g. hipMemset).  Every completed call leaves its counter region zero
- * again, so later calls need no clearing.  Contents are otherwise scratch.
+ * The workspace is scratch: no initialisation is needed and its contents are
+ * meaningless between calls.
  */
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
                                         int32_t gqa_group, int32_t head_dim,
@@ -127,7 +126,8 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
  *   gqa_group     1 .. 16
  *   workspace     >= paged_attn_decode_workspace_size(..., 0) bytes
  * The work over all (sequence, kv head, block) triples is split evenly across
- * the GPU, partial results are merged by log-sum-exp inside the same launch.
+ * the GPU; partial results of split sequences are merged by log-sum-exp in a
+ * second launch on the same stream.
  * A sequence with context length 0 gets out = 0 and lse = -inf.
  */
 int paged_attn_decode(void* out, float* lse, const void* q, const void* k_pool,

@@ -108,13 +108,13 @@ def test_decode_empty_sequences():
 
 
 def test_decode_workspace_reused_across_calls():
-    """Counters must be left at zero: two calls in a row on one workspace,
+    """One workspace for many calls in a row (no clearing between them),
     the second with a smaller batch, both correct."""
     big = wl.make_decode_case(321, [3000, 17, 900, 2048, 5], 8, 2, 128, "bf16", softcap=20.0)
     small = wl.make_decode_case(322, [100, 1500], 8, 2, 128, "bf16")
     need = max(pkv.paged_attn_decode_workspace_size(5, 2, 4, 128, 3000, 0),
                pkv.paged_attn_decode_workspace_size(5, 2, 4, 128, 3000, 64))
-    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # garbage, not zeros
     for mode, P in (("balanced", None), ("splitk", 64)):
         for case in (big, small, big):
             banner("decode reuse", mode, case.context_lens.tolist())
