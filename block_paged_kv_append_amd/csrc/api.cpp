@@ -306,7 +306,7 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q
   a.window = window > 0 ? window : 0;
   a.scale = scale;
   a.softcap = softcap > 0.f ? softcap : 0.f;
-  const int per_item = 4 * pkv::prefill_row_tiles(head_dim) * (16 / gqa_group);
+  const int per_item = 4 * pkv::prefill_row_tiles(head_dim, dtype == PKV_BF16) * (16 / gqa_group);
   a.tiles_per_seq = (max_q_len + per_item - 1) / per_item;
   const long long items = (long long)num_seqs * num_kv_heads * a.tiles_per_seq;
   if (items > INT_MAX) return fail(PKV_EINVAL, "%s: %lld work items exceed the grid limit", fn, items);

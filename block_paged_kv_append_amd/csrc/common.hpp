@@ -17,6 +17,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 // ---------------------------------------------------------------------------
 // matrix-core operations (operand layouts, lane = 16 * j + c):
@@ -32,6 +33,13 @@ __device__ __forceinline__ f32x4 mma_bf16_k32(u32x4 a, u32x4 b, f32x4 c) {
 __device__ __forceinline__ f32x4 mma_bf16_k16(u32x2 a, u32x2 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a),
                                                     __builtin_bit_cast(i16x4, b), c, 0, 0, 0);
+}
+// 32x32 output tile, k = 16: A lane (row l%32) holds A[row][8*(l/32) + 0..7],
+// B lane (col l%32) holds B[8*(l/32) + 0..7][col], C element v of lane l is
+// C[8*(v/4) + 4*(l/32) + v%4][l%32].
+__device__ __forceinline__ f32x16 mma32_bf16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x4 mma_f32_k4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -60,6 +68,23 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return bf16_rne(lo) | (bf16_rne(hi) << 16);
+}
+
+// round-to-nearest-even bf16 pair by the hardware conversion
+__device__ __forceinline__ uint32_t pack_bf16x2_hw(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// x combined with the value of lane l ^ 32 (one cross-half lane swap)
+__device__ __forceinline__ float half_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // ---------------------------------------------------------------------------

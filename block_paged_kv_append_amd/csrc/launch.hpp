@@ -84,6 +84,6 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, hipStream_t stream);
 
 // Row tiles (of 16 GQA-packed query rows) per wave in the prefill kernel.
-int prefill_row_tiles(int head_dim);
+int prefill_row_tiles(int head_dim, bool bf16);
 
 }  // namespace pkv

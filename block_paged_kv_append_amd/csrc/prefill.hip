@@ -177,6 +177,263 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 form on 32x32x16 matrix-core tiles.
+//
+// A wave owns 32 GQA-packed query rows (32 / G positions times G heads); the
+// four waves of a workgroup cover consecutive positions of one (sequence, kv
+// head).  Keys are taken 32 at a time (two cache blocks, a "stage"):
+//   S^T[32 keys][32 rows] = K Q^T         (D/16 products, k = 16 dims)
+//   O^T[D][32 rows]      += V^T P^T       (D/32 row tiles x 2 blocks, k = 16 keys)
+// Computing O transposed keeps a row's statistics (max, sum, rescale factor)
+// in the two lanes that hold that row's scores, so the softmax needs one
+// cross-half lane swap per stage and no other exchange.
+//
+// K/V reach LDS by direct global->LDS copies (16 bytes per lane, a wave
+// writes 1 KiB contiguous, each lane picks its own source).  The copy lays
+// every stage out in the order the matrix cores consume it, so each operand
+// is one linear 1 KiB LDS read:
+//   K run s (s < D/16): lane (i, kg) <- K[block i/16][token pi(i%16)][dims 16s + 8kg .. +7]
+//   V run 2x+q:         lane (i, kg) <- V[block q][tokens 8kg .. +7][dim 32x + i]
+// where pi swaps bits 2 and 3 of the token index, which makes the score tile's
+// register v of lane (n, kg) the score of key 16*(v/8) + 8kg + v%8: the same
+// lane then holds, per block, exactly the 8 probabilities the V^T P^T product
+// wants from it.  NB stage buffers form a ring; copies run NB-2 stages ahead
+// and each stage costs one barrier.  The next stage's S^T is computed before
+// the current stage's softmax and P V, so matrix-core and vector work overlap.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+__device__ __forceinline__ void copy_to_lds(const u32x4* src, u32x4* wave_dst) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)wave_dst, 16, 0, 0);
+}
+
+template <int D, int NB>
+__global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs a) {
+  constexpr int KD = D / 16;                    // K runs per stage = QK products
+  constexpr int XT = D / 32;                    // output row tiles of O^T
+  constexpr int kRuns = KD + 2 * XT;            // 1 KiB runs per stage
+  constexpr int kStageU4 = kRuns * kWave;       // 16-byte chunks per stage
+  constexpr int kDma = kRuns / kWaves;          // copies per wave per stage
+  constexpr int kTileU4 = D * kBlock * 2 / 16;  // chunks of one block's K (or V) in the pool
+  static_assert(KD % kWaves == 0 && (2 * XT) % kWaves == 0, "runs must split over the waves");
+  static_assert(NB >= 3 && (NB & (NB - 1)) == 0, "ring of 4 or 8 stages");
+  __shared__ u32x4 smem[NB * kStageU4];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n = lane & 31, kg = lane >> 5;
+  const int G = a.gqa_group, Hkv = a.num_kv_heads, Hq = G * Hkv;
+  const int PPW = 32 / G;  // positions per wave
+  const LogitXform xf = make_xform(a.scale, a.softcap);
+
+  int item = blockIdx.x;
+  if (a.num_items % 8 == 0) item = (blockIdx.x % 8) * (a.num_items / 8) + blockIdx.x / 8;
+  const int tile = item % a.tiles_per_seq;
+  const int bg = item / a.tiles_per_seq;
+  const int g = bg % Hkv, b = bg / Hkv;
+
+  const int L = min(max(a.context_lens[b], 0), a.max_blocks_per_seq * kBlock);
+  const int r0 = min(max(a.cu_q_lens[b], 0), a.num_q_tokens);
+  const int r1 = min(max(a.cu_q_lens[b + 1], r0), a.num_q_tokens);
+  const int nq = r1 - r0;
+  const int pos_wg = tile * (kWaves * PPW);
+  if (pos_wg >= nq) return;  // whole workgroup, before any barrier
+  const int shift = L - nq;
+  const int pos_wave = pos_wg + wave * PPW;
+  const bool wave_live = pos_wave < nq;
+  const int pos = pos_wave + n / G;
+  const bool rvalid = pos < nq;
+  const int qpos = shift + pos;
+  const int head = g * G + n % G;
+  // positions of the wave's first and last real row (uniform)
+  const int qpos_lo = shift + pos_wave;
+  const int qpos_hi = shift + min(pos_wave + PPW - 1, nq - 1);
+
+  u32x4 qf[KD];
+  {
+    const uint16_t* row =
+        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)(r0 + min(pos, nq - 1)) * Hq + head) * D + 8 * kg;
+#pragma unroll
+    for (int i = 0; i < KD; ++i) qf[i] = *reinterpret_cast<const u32x4*>(row + 16 * i);
+  }
+
+  // keys the workgroup's rows can see
+  const int p_hi = min(nq - 1, pos_wg + kWaves * PPW - 1);
+  const int last_tok = min(shift + p_hi, L - 1);
+  if (last_tok < 0) return;
+  const int first_tok = a.window > 0 ? max(0, shift + pos_wg - a.window + 1) : 0;
+  const int blk_lo = first_tok / kBlock;
+  const int nblk = last_tok / kBlock - blk_lo + 1;
+  const int nstage = (nblk + 1) / 2;
+  const int* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk_lo;
+  const u32x4* kpool = reinterpret_cast<const u32x4*>(a.k_pool);
+  const u32x4* vpool = reinterpret_cast<const u32x4*>(a.v_pool);
+
+  // per-lane source offsets of the copies (see the layout above)
+  const int k_off = 16 * kg + ((n & 3) | ((n & 4) << 1) | ((n & 8) >> 1));
+  const bool k_hi = n >= 16;
+  const int v_off = 2 * n + kg;
+
+  int tbl = 0, tbl_base = -64;
+  uint32_t okbits = 0;  // bit 2 * (stage % NB) + q: block q of that stage is readable
+  auto issue = [&](int st) {
+    size_t base[2];
+    uint32_t ok2 = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int lb = 2 * st + q;
+      if (lb - tbl_base >= 64) {  // uniform
+        tbl_base = lb & ~63;
+        tbl = (tbl_base + lane < nblk) ? bt[tbl_base + lane] : 0;
+      }
+      const int phys = __builtin_amdgcn_readlane(tbl, lb - tbl_base);
+      const bool ok = lb < nblk && (unsigned)phys < (unsigned)a.num_blocks;
+      ok2 |= (uint32_t)ok << q;
+      base[q] = ((size_t)(ok ? phys : 0) * Hkv + g) * kTileU4;  // unreadable: block 0, masked
+    }
+    const int slot = st & (NB - 1);
+    okbits = (okbits & ~(3u << (2 * slot))) | (ok2 << (2 * slot));
+    u32x4* dst = smem + slot * kStageU4;
+    const u32x4* ksrc = kpool + (k_hi ? base[1] : base[0]) + k_off;
+#pragma unroll
+    for (int e = 0; e < KD / kWaves; ++e) {
+      const int s = e * kWaves + wave;
+      copy_to_lds(ksrc + 32 * s, dst + s * kWave);
+    }
+    const u32x4* vsrc = vpool + base[wave & 1] + v_off;
+#pragma unroll
+    for (int e = 0; e < 2 * XT / kWaves; ++e) {
+      const int x = 2 * e + (wave >> 1);
+      copy_to_lds(vsrc + 64 * x, dst + (KD + 2 * x + (wave & 1)) * kWave);
+    }
+  };
+
+  auto qk = [&](int st) {
+    const u32x4* kb = smem + (st & (NB - 1)) * kStageU4 + lane;
+    f32x16 sc = {};
+#pragma unroll
+    for (int i = 0; i < KD; ++i) sc = mma32_bf16(kb[i * kWave], qf[i], sc);
+    return sc;
+  };
+
+  f32x16 o[XT];
+#pragma unroll
+  for (int x = 0; x < XT; ++x) o[x] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  constexpr float kLazy = 8.0f;
+
+  // step k: softmax of stage k's scores, then O^T += V^T P^T
+  auto step = [&](int k, const f32x16& sc) {
+    const int tok0 = (blk_lo + 2 * k) * kBlock;
+    const uint32_t okk = (okbits >> (2 * (k & (NB - 1)))) & 3u;
+    const bool full = okk == 3u && tok0 + 31 < L && tok0 + 31 <= qpos_lo &&
+                      (a.window <= 0 || qpos_hi - tok0 < a.window);
+    float s[16];
+    if (xf.cap > 0.f) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = softcap_log2(sc[v] * xf.scale, xf.cap, xf.inv_cap);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s[v] = sc[v] * xf.scale_log2;
+    }
+    if (!full) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tk = tok0 + 16 * (v >> 3) + 8 * kg + (v & 7);
+        const bool vis = ((okk >> (v >> 3)) & 1u) & rvalid & (tk < L) & (tk <= qpos) &
+                         ((a.window <= 0) | (qpos - tk < a.window));
+        s[v] = vis ? s[v] : kNegInf;
+      }
+    }
+    float mx = s[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+    mx = half_max(mx);
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int x = 0; x < XT; ++x) o[x] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    float p[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p[v] = fast_exp2(s[v] - m_use);
+    float ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ls += p[v];
+    l_run += ls;
+    u32x4 pb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      pb[q] = u32x4{pack_bf16x2_hw(p[8 * q + 0], p[8 * q + 1]), pack_bf16x2_hw(p[8 * q + 2], p[8 * q + 3]),
+                    pack_bf16x2_hw(p[8 * q + 4], p[8 * q + 5]), pack_bf16x2_hw(p[8 * q + 6], p[8 * q + 7])};
+    const u32x4* vb = smem + (k & (NB - 1)) * kStageU4 + KD * kWave + lane;
+    // keys past the context (or of an unreadable block) may hold anything
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int nv = full ? 16 : (((okk >> q) & 1u) ? L - (tok0 + 16 * q) - 8 * kg : 0);
+      const u32x4 vm = {(0 < nv ? 0x0000FFFFu : 0u) | (1 < nv ? 0xFFFF0000u : 0u),
+                        (2 < nv ? 0x0000FFFFu : 0u) | (3 < nv ? 0xFFFF0000u : 0u),
+                        (4 < nv ? 0x0000FFFFu : 0u) | (5 < nv ? 0xFFFF0000u : 0u),
+                        (6 < nv ? 0x0000FFFFu : 0u) | (7 < nv ? 0xFFFF0000u : 0u)};
+#pragma unroll
+      for (int x = 0; x < XT; ++x) o[x] = mma32_bf16(vb[(2 * x + q) * kWave] & vm, pb[q], o[x]);
+    }
+  };
+
+#pragma unroll
+  for (int st = 0; st < NB - 1; ++st) issue(st);
+  wait_vmem<(NB - 2) * kDma>();
+  lds_barrier();
+  // stage k: wait for stage k + 1, refill the ring, S^T of stage k + 1 into
+  // `next`, then softmax and P V of stage k from `cur`.  Two stages per trip
+  // so that the score tiles swap roles without register copies.
+  auto iter = [&](int k, const f32x16& cur, f32x16& next) {
+    wait_vmem<(NB - 3) * kDma>();  // stage k + 1 has landed (this wave's part)
+    lds_barrier();                 // ... and every other wave's
+    issue(k + NB - 1);             // into the slot stage k - 1 used
+    if (wave_live) {
+      if (k + 1 < nstage) next = qk(k + 1);
+      mma_result_fence();
+      step(k, cur);
+    }
+  };
+  f32x16 s0 = {}, s1 = {};
+  if (wave_live) s0 = qk(0);
+  for (int k = 0; k < nstage; k += 2) {
+    iter(k, s0, s1);
+    if (k + 1 < nstage) iter(k + 1, s1, s0);
+  }
+  wait_vmem<0>();  // no copy may still be in flight when the workgroup ends
+  mma_result_fence();
+  if (!wave_live) return;
+
+  const float l_tot = half_sum(l_run);
+  if (a.lse != nullptr && kg == 0 && rvalid)
+    a.lse[(size_t)(r0 + pos) * Hq + head] = l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
+  if (!rvalid) return;
+  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)(r0 + pos) * Hq + head) * D + 4 * kg;
+#pragma unroll
+  for (int x = 0; x < XT; ++x)
+#pragma unroll
+    for (int h = 0; h < 4; ++h)
+      *reinterpret_cast<u32x2*>(dst + 32 * x + 8 * h) =
+          u32x2{pack_bf16x2_hw(o[x][4 * h] * inv, o[x][4 * h + 1] * inv),
+                pack_bf16x2_hw(o[x][4 * h + 2] * inv, o[x][4 * h + 3] * inv)};
+}
+
 template <bool BF16, int D, int RT>
 hipError_t launch_p(PrefillArgs a, hipStream_t stream) {
   const int pos_per_item = kWaves * RT * (16 / a.gqa_group);
@@ -188,17 +445,26 @@ hipError_t launch_p(PrefillArgs a, hipStream_t stream) {
 
 }  // namespace
 
-// Row tiles per wave: two at head_dim 64/128, one at 256 (register budget).
-int prefill_row_tiles(int head_dim) { return head_dim >= 256 ? 1 : 2; }
+// Row tiles per wave of the bf16 (LDS) form, and of the fp32 form.
+#ifndef PKV_PREFILL_RING
+#define PKV_PREFILL_RING 4
+#endif
+int prefill_row_tiles(int head_dim, bool bf16) {
+  if (bf16) return 2;  // 32 rows per wave
+  return head_dim >= 256 ? 1 : 2;
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, hipStream_t stream) {
   if (a.num_items <= 0) return hipSuccess;
   if (bf16) {
+    hipError_t e = hipSuccess;
     switch (head_dim) {
-      case 64: return launch_p<true, 64, 2>(a, stream);
-      case 128: return launch_p<true, 128, 2>(a, stream);
-      case 256: return launch_p<true, 256, 1>(a, stream);
+      case 64: prefill_mma32_kernel<64, PKV_PREFILL_RING><<<a.num_items, kThreads, 0, stream>>>(a); break;
+      case 128: prefill_mma32_kernel<128, PKV_PREFILL_RING><<<a.num_items, kThreads, 0, stream>>>(a); break;
+      case 256: prefill_mma32_kernel<256, PKV_PREFILL_RING><<<a.num_items, kThreads, 0, stream>>>(a); break;
+      default: e = hipErrorInvalidValue;
     }
+    return e != hipSuccess ? e : hipGetLastError();
   } else {
     switch (head_dim) {
       case 64: return launch_p<false, 64, 2>(a, stream);
