@@ -211,11 +211,42 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
-__device__ __forceinline__ void copy_to_lds(const u32x4* src, u32x4* wave_dst) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)wave_dst, 16, 0, 0);
+__device__ __forceinline__ void wait_lds() {
+  __builtin_amdgcn_s_waitcnt((15) | (3 << 14) | (7 << 4) | (0 << 8));  // lgkmcnt(0) only
+}
+// Issue order for a region of NMF matrix-core products fed by NMF LDS
+// operand reads: the reads run four products ahead, NVA vector
+// instructions sit in each product's shadow.
+template <int NMF, int NVA>
+__device__ __forceinline__ void pipeline_order() {
+  constexpr int kAhead = NMF < 4 ? NMF : 4;
+  __builtin_amdgcn_sched_group_barrier(0x100, kAhead, 0);
+#pragma unroll
+  for (int i = 0; i < NMF - kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NVA, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(0x002, NVA, 0);
+  }
+}
+// buffer resource of one block's K (or V) tile: a raw byte range, empty when
+// the block may not be read (copies then return zeros)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, int bytes) {
+  constexpr unsigned kRawBufferWord3 = 0x00020000u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRawBufferWord3);
+}
+// 16 bytes per lane from the buffer into LDS; a wave writes 1 KiB starting at
+// wave_dst, lane i at +16 i.  A buffer (not global) copy: the compiler's LDS
+// wait counting stays exact around it.
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int byte_off, u32x4* wave_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)wave_dst, 16, byte_off, 0, 0, 0);
 }
 
-template <int D, int NB>
+template <int D, int NB, bool SC>
 __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs a) {
   constexpr int KD = D / 16;                    // K runs per stage = QK products
   constexpr int XT = D / 32;                    // output row tiles of O^T
@@ -263,6 +294,11 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
         reinterpret_cast<const uint16_t*>(a.q) + ((size_t)(r0 + min(pos, nq - 1)) * Hq + head) * D + 8 * kg;
 #pragma unroll
     for (int i = 0; i < KD; ++i) qf[i] = *reinterpret_cast<const u32x4*>(row + 16 * i);
+    // the query fragments live in the accumulator file (the matrix cores
+    // read operands from either file), leaving vector registers for operand
+    // prefetch
+#pragma unroll
+    for (int i = 0; i < KD; ++i) asm volatile("" : "=a"(qf[i]) : "0"(qf[i]));
   }
 
   // keys the workgroup's rows can see
@@ -277,87 +313,119 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
   const u32x4* kpool = reinterpret_cast<const u32x4*>(a.k_pool);
   const u32x4* vpool = reinterpret_cast<const u32x4*>(a.v_pool);
 
-  // per-lane source offsets of the copies (see the layout above)
-  const int k_off = 16 * kg + ((n & 3) | ((n & 4) << 1) | ((n & 8) >> 1));
-  const bool k_hi = n >= 16;
+  // per-lane chunk offsets of the copies within a block (see the layout above)
+  const int k_off = 16 * (lane >> 4) + ((lane & 3) | ((lane & 4) << 1) | ((lane & 8) >> 1));
   const int v_off = 2 * n + kg;
+  // where lane (n, kg) finds its K operand inside a pair of runs
+  const int k_rd = ((n >> 4) << 6) + (n & 15) + 16 * kg;
 
-  int tbl = 0, tbl_base = -64;
+  // table entries are uniform: scalar loads, which leave the vector memory
+  // counter (the ring's copies) alone
+  typedef const __attribute__((address_space(4))) int* const_int_ptr;
+  const const_int_ptr btc = (const_int_ptr)bt;
   uint32_t okbits = 0;  // bit 2 * (stage % NB) + q: block q of that stage is readable
   auto issue = [&](int st) {
-    size_t base[2];
     uint32_t ok2 = 0;
+    // consumed at once: no scalar load may stay in flight across the
+    // compute phases, whose LDS waits could then not count partially
+    const int cur[2] = {btc[min(2 * st, nblk - 1)], btc[min(2 * st + 1, nblk - 1)]};
+    __amdgpu_buffer_rsrc_t rk[2], rv[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int lb = 2 * st + q;
-      if (lb - tbl_base >= 64) {  // uniform
-        tbl_base = lb & ~63;
-        tbl = (tbl_base + lane < nblk) ? bt[tbl_base + lane] : 0;
-      }
-      const int phys = __builtin_amdgcn_readlane(tbl, lb - tbl_base);
-      const bool ok = lb < nblk && (unsigned)phys < (unsigned)a.num_blocks;
+      const bool ok = lb < nblk && (unsigned)cur[q] < (unsigned)a.num_blocks;
       ok2 |= (uint32_t)ok << q;
-      base[q] = ((size_t)(ok ? phys : 0) * Hkv + g) * kTileU4;  // unreadable: block 0, masked
+      const size_t off = ((size_t)(ok ? cur[q] : 0) * Hkv + g) * kTileU4;
+      // an unreadable block gets an empty range: its copies read zeros
+      rk[q] = tile_rsrc(kpool + off, ok ? kTileU4 * 16 : 0);
+      rv[q] = tile_rsrc(vpool + off, ok ? kTileU4 * 16 : 0);
     }
     const int slot = st & (NB - 1);
     okbits = (okbits & ~(3u << (2 * slot))) | (ok2 << (2 * slot));
     u32x4* dst = smem + slot * kStageU4;
-    const u32x4* ksrc = kpool + (k_hi ? base[1] : base[0]) + k_off;
+    // K runs 2p, 2p+1 form 2 KiB: the first KiB from block 0 (run 2p's lanes
+    // n < 16, then run 2p+1's), the second from block 1; each copy reads
+    // one block
 #pragma unroll
     for (int e = 0; e < KD / kWaves; ++e) {
-      const int s = e * kWaves + wave;
-      copy_to_lds(ksrc + 32 * s, dst + s * kWave);
+      const int pr = 2 * e + (wave >> 1), blk = wave & 1;
+      copy_to_lds(rk[blk], (64 * pr + k_off) * 16, dst + pr * 2 * kWave + blk * kWave);
     }
-    const u32x4* vsrc = vpool + base[wave & 1] + v_off;
 #pragma unroll
     for (int e = 0; e < 2 * XT / kWaves; ++e) {
       const int x = 2 * e + (wave >> 1);
-      copy_to_lds(vsrc + 64 * x, dst + (KD + 2 * x + (wave & 1)) * kWave);
+      copy_to_lds(rv[wave & 1], (64 * x + v_off) * 16, dst + (KD + 2 * x + (wave & 1)) * kWave);
     }
   };
 
-  auto qk = [&](int st) {
-    const u32x4* kb = smem + (st & (NB - 1)) * kStageU4 + lane;
-    f32x16 sc = {};
+  // chunk offset of K run s within a stage, relative to k_rd
+  auto k_run = [](int s) { return (s >> 1) * 2 * kWave + (s & 1) * 32; };
+  auto stage_tok0 = [&](int st) { return (blk_lo + 2 * st) * kBlock; };
+  auto stage_ok = [&](int st) { return (okbits >> (2 * (st & (NB - 1)))) & 3u; };
+  // every score of the stage is visible to every real row of this wave
+  auto stage_full = [&](int st) {
+    const int tok0 = stage_tok0(st);
+    return stage_ok(st) == 3u && tok0 + 31 < L && tok0 + 31 <= qpos_lo &&
+           (a.window <= 0 || qpos_hi - tok0 < a.window);
+  };
+  // Keys past the context (or of an unreadable block) may hold anything; in
+  // LDS their V entries are cleared once the stage has landed, so that the
+  // products never multiply a zero probability by a non-finite value.  Rare
+  // (the context's last block), done by the whole workgroup.
+  auto clear_v_tail = [&](int st) {
+    const int tok0 = stage_tok0(st);
+    const uint32_t okk = stage_ok(st);
+    if (okk == 3u && tok0 + 2 * kBlock <= L) return;
+    u32x4* vr = smem + (st & (NB - 1)) * kStageU4 + KD * kWave;
+    for (int c = threadIdx.x; c < 2 * XT * kWave; c += kThreads) {
+      const int q = (c >> 6) & 1, kgc = (c >> 5) & 1;
+      const int nv = ((okk >> q) & 1u) ? L - (tok0 + 16 * q) - 8 * kgc : 0;
+      if (nv >= 8) continue;
+      const u32x4 m = {(0 < nv ? 0x0000FFFFu : 0u) | (1 < nv ? 0xFFFF0000u : 0u),
+                       (2 < nv ? 0x0000FFFFu : 0u) | (3 < nv ? 0xFFFF0000u : 0u),
+                       (4 < nv ? 0x0000FFFFu : 0u) | (5 < nv ? 0xFFFF0000u : 0u),
+                       (6 < nv ? 0x0000FFFFu : 0u) | (7 < nv ? 0xFFFF0000u : 0u)};
+      vr[c] = vr[c] & m;
+    }
+    wait_lds();  // written before this wave reaches the next barrier
+  };
+  // score (raw S^T element v of stage st) -> -inf where not visible
+  auto mask_scores = [&](int st, f32x16& sc) {
+    const int tok0 = stage_tok0(st);
+    const uint32_t okk = stage_ok(st);
 #pragma unroll
-    for (int i = 0; i < KD; ++i) sc = mma32_bf16(kb[i * kWave], qf[i], sc);
-    return sc;
+    for (int v = 0; v < 16; ++v) {
+      const int tk = tok0 + 16 * (v >> 3) + 8 * kg + (v & 7);
+      const bool vis = ((okk >> (v >> 3)) & 1u) & rvalid & (tk < L) & (tk <= qpos) &
+                       ((a.window <= 0) | (qpos - tk < a.window));
+      sc[v] = vis ? sc[v] : kNegInf;
+    }
+  };
+  // base-2 logit; a masked score stays -inf
+  auto logit = [&](float x) {
+    if constexpr (SC) {
+      const float y = softcap_log2(x * xf.scale, xf.cap, xf.inv_cap);
+      return x == kNegInf ? kNegInf : y;
+    } else {
+      return x * xf.scale_log2;
+    }
   };
 
   f32x16 o[XT];
 #pragma unroll
   for (int x = 0; x < XT; ++x) o[x] = f32x16{};
   float m_run = kNegInf, l_run = 0.f;
-  constexpr float kLazy = 8.0f;
+  constexpr float kLazy = 8.0f;  // rescale only when the max grows by 2^8
+  float sv[16];                  // base-2 logits of the stage to exponentiate next
 
-  // step k: softmax of stage k's scores, then O^T += V^T P^T
-  auto step = [&](int k, const f32x16& sc) {
-    const int tok0 = (blk_lo + 2 * k) * kBlock;
-    const uint32_t okk = (okbits >> (2 * (k & (NB - 1)))) & 3u;
-    const bool full = okk == 3u && tok0 + 31 < L && tok0 + 31 <= qpos_lo &&
-                      (a.window <= 0 || qpos_hi - tok0 < a.window);
-    float s[16];
-    if (xf.cap > 0.f) {
+  // new row maxima: grow the running max (rarely) and rescale what is summed
+  auto update_max = [&]() {
+    float mx = sv[0];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = softcap_log2(sc[v] * xf.scale, xf.cap, xf.inv_cap);
-    } else {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s[v] = sc[v] * xf.scale_log2;
-    }
-    if (!full) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int tk = tok0 + 16 * (v >> 3) + 8 * kg + (v & 7);
-        const bool vis = ((okk >> (v >> 3)) & 1u) & rvalid & (tk < L) & (tk <= qpos) &
-                         ((a.window <= 0) | (qpos - tk < a.window));
-        s[v] = vis ? s[v] : kNegInf;
-      }
-    }
-    float mx = s[0];
-#pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, s[v]);
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sv[v]);
     mx = half_max(mx);
     if (__any(mx > m_run + kLazy)) {
+      mma_result_fence();
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
       l_run *= alpha;
@@ -365,55 +433,106 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
       for (int x = 0; x < XT; ++x) o[x] *= alpha;
       m_run = m_new;
     }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float p[16];
-#pragma unroll
-    for (int v = 0; v < 16; ++v) p[v] = fast_exp2(s[v] - m_use);
-    float ls = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) ls += p[v];
-    l_run += ls;
-    u32x4 pb[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-      pb[q] = u32x4{pack_bf16x2_hw(p[8 * q + 0], p[8 * q + 1]), pack_bf16x2_hw(p[8 * q + 2], p[8 * q + 3]),
-                    pack_bf16x2_hw(p[8 * q + 4], p[8 * q + 5]), pack_bf16x2_hw(p[8 * q + 6], p[8 * q + 7])};
-    const u32x4* vb = smem + (k & (NB - 1)) * kStageU4 + KD * kWave + lane;
-    // keys past the context (or of an unreadable block) may hold anything
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int nv = full ? 16 : (((okk >> q) & 1u) ? L - (tok0 + 16 * q) - 8 * kg : 0);
-      const u32x4 vm = {(0 < nv ? 0x0000FFFFu : 0u) | (1 < nv ? 0xFFFF0000u : 0u),
-                        (2 < nv ? 0x0000FFFFu : 0u) | (3 < nv ? 0xFFFF0000u : 0u),
-                        (4 < nv ? 0x0000FFFFu : 0u) | (5 < nv ? 0xFFFF0000u : 0u),
-                        (6 < nv ? 0x0000FFFFu : 0u) | (7 < nv ? 0xFFFF0000u : 0u)};
-#pragma unroll
-      for (int x = 0; x < XT; ++x) o[x] = mma32_bf16(vb[(2 * x + q) * kWave] & vm, pb[q], o[x]);
-    }
   };
 
 #pragma unroll
   for (int st = 0; st < NB - 1; ++st) issue(st);
   wait_vmem<(NB - 2) * kDma>();
   lds_barrier();
-  // stage k: wait for stage k + 1, refill the ring, S^T of stage k + 1 into
-  // `next`, then softmax and P V of stage k from `cur`.  Two stages per trip
-  // so that the score tiles swap roles without register copies.
-  auto iter = [&](int k, const f32x16& cur, f32x16& next) {
+  clear_v_tail(0);
+  lds_barrier();
+  if (wave_live) {
+    const u32x4* kb = smem + k_rd;
+    f32x16 acc = {};
+#pragma unroll
+    for (int i = 0; i < KD; ++i) acc = mma32_bf16(kb[k_run(i)], qf[i], acc);
+    mma_result_fence();
+    if (!stage_full(0)) mask_scores(0, acc);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) sv[v] = logit(acc[v]);
+    update_max();
+  }
+
+  // Stage k, in two phases without branches:
+  //   1: S^T of stage k + 1 on the matrix cores  |  exponentials of stage k
+  //   2: O^T += V^T P^T of stage k               |  logits and max of stage k + 1
+  // Operand reads run up to four products ahead of their use.  The last trip
+  // computes the scores of a dummy stage: fully masked, never used.
+  for (int k = 0; k < nstage; ++k) {
     wait_vmem<(NB - 3) * kDma>();  // stage k + 1 has landed (this wave's part)
     lds_barrier();                 // ... and every other wave's
-    issue(k + NB - 1);             // into the slot stage k - 1 used
-    if (wave_live) {
-      if (k + 1 < nstage) next = qk(k + 1);
-      mma_result_fence();
-      step(k, cur);
+    if (k + 1 < nstage) clear_v_tail(k + 1);
+    issue(k + NB - 1);  // into the slot stage k - 1 used
+    if (!wave_live) continue;
+
+    // phase 1: the order below is the issue order (scheduling barriers)
+    constexpr int kE = 16 / KD;  // score elements handled per product
+    const u32x4* kb = smem + ((k + 1) & (NB - 1)) * kStageU4 + k_rd;
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    f32x16 acc = {};
+    float p[16];
+    {
+      u32x4 kf[4];
+#pragma unroll
+      for (int i = 0; i < 4 && i < KD; ++i) kf[i] = kb[k_run(i)];
+#pragma unroll
+      for (int i = 0; i < KD; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mma32_bf16(kf[i & 3], qf[i], acc);
+        if (i + 4 < KD) kf[i & 3] = kb[k_run(i + 4)];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) p[i * kE + e] = fast_exp2(sv[i * kE + e] - m_use);
+      }
     }
-  };
-  f32x16 s0 = {}, s1 = {};
-  if (wave_live) s0 = qk(0);
-  for (int k = 0; k < nstage; k += 2) {
-    iter(k, s0, s1);
-    if (k + 1 < nstage) iter(k + 1, s1, s0);
+    __builtin_amdgcn_sched_barrier(0);
+    float ls = 0.f;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) ls += p[v];
+    l_run += ls;
+    u32x4 pb[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      pb[q] = u32x4{pack_bf16x2_hw(p[8 * q + 0], p[8 * q + 1]), pack_bf16x2_hw(p[8 * q + 2], p[8 * q + 3]),
+                    pack_bf16x2_hw(p[8 * q + 4], p[8 * q + 5]), pack_bf16x2_hw(p[8 * q + 6], p[8 * q + 7])};
+      asm volatile("" ::"v"(pb[q]));  // computed here, not sunk into phase 2
+    }
+    asm volatile("" ::"v"(l_run));
+
+    mma_result_fence();
+    if (!stage_full(k + 1)) mask_scores(k + 1, acc);
+
+    // phase 2
+    const u32x4* vb = smem + (k & (NB - 1)) * kStageU4 + KD * kWave + lane;
+    {
+      constexpr int NU = 2 * XT;  // products: u = q * XT + x
+      u32x4 vf[4];
+#pragma unroll
+      for (int u = 0; u < 4 && u < NU; ++u) vf[u] = vb[(2 * (u % XT) + u / XT) * kWave];
+      float mx = kNegInf;
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int x = u % XT, q = u / XT;
+        o[x] = mma32_bf16(vf[u & 3], pb[q], o[x]);
+        if (u + 4 < NU) vf[u & 3] = vb[(2 * ((u + 4) % XT) + (u + 4) / XT) * kWave];
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+          sv[u * kE + e] = logit(acc[u * kE + e]);
+          mx = fmaxf(mx, sv[u * kE + e]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mx = half_max(mx);
+      if (__any(mx > m_run + kLazy)) {
+        mma_result_fence();
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int x2 = 0; x2 < XT; ++x2) o[x2] *= alpha;
+        m_run = m_new;
+      }
+    }
   }
   wait_vmem<0>();  // no copy may still be in flight when the workgroup ends
   mma_result_fence();
@@ -434,6 +553,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
                 pack_bf16x2_hw(o[x][4 * h + 2] * inv, o[x][4 * h + 3] * inv)};
 }
 
+#ifndef PKV_PREFILL_RING
+#define PKV_PREFILL_RING 4
+#endif
+template <int D>
+void launch_mma32(PrefillArgs a, hipStream_t stream) {
+  if (a.softcap > 0.f)
+    prefill_mma32_kernel<D, PKV_PREFILL_RING, true><<<a.num_items, kThreads, 0, stream>>>(a);
+  else
+    prefill_mma32_kernel<D, PKV_PREFILL_RING, false><<<a.num_items, kThreads, 0, stream>>>(a);
+}
+
 template <bool BF16, int D, int RT>
 hipError_t launch_p(PrefillArgs a, hipStream_t stream) {
   const int pos_per_item = kWaves * RT * (16 / a.gqa_group);
@@ -446,9 +576,6 @@ hipError_t launch_p(PrefillArgs a, hipStream_t stream) {
 }  // namespace
 
 // Row tiles per wave of the bf16 (LDS) form, and of the fp32 form.
-#ifndef PKV_PREFILL_RING
-#define PKV_PREFILL_RING 4
-#endif
 int prefill_row_tiles(int head_dim, bool bf16) {
   if (bf16) return 2;  // 32 rows per wave
   return head_dim >= 256 ? 1 : 2;
@@ -459,9 +586,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, hipStre
   if (bf16) {
     hipError_t e = hipSuccess;
     switch (head_dim) {
-      case 64: prefill_mma32_kernel<64, PKV_PREFILL_RING><<<a.num_items, kThreads, 0, stream>>>(a); break;
-      case 128: prefill_mma32_kernel<128, PKV_PREFILL_RING><<<a.num_items, kThreads, 0, stream>>>(a); break;
-      case 256: prefill_mma32_kernel<256, PKV_PREFILL_RING><<<a.num_items, kThreads, 0, stream>>>(a); break;
+      case 64: launch_mma32<64>(a, stream); break;
+      case 128: launch_mma32<128>(a, stream); break;
+      case 256: launch_mma32<256>(a, stream); break;
       default: e = hipErrorInvalidValue;
     }
     return e != hipSuccess ? e : hipGetLastError();
