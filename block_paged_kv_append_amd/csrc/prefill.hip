@@ -319,16 +319,23 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
   // where lane (n, kg) finds its K operand inside a pair of runs
   const int k_rd = ((n >> 4) << 6) + (n & 15) + 16 * kg;
 
-  // table entries are uniform: scalar loads, which leave the vector memory
-  // counter (the ring's copies) alone
-  typedef const __attribute__((address_space(4))) int* const_int_ptr;
-  const const_int_ptr btc = (const_int_ptr)bt;
-  uint32_t okbits = 0;  // bit 2 * (stage % NB) + q: block q of that stage is readable
+  // Block-table entries, 64 per vector register (lane i: entry base + i),
+  // the next slice loaded one slice ahead; read out with a lane select.
+  int tbl_cur = lane < nblk ? bt[lane] : 0;
+  int tbl_nxt = 64 + lane < nblk ? bt[64 + lane] : 0;
+  int tbl_base = 0;
+  uint32_t okbits = 0;    // bit 2 * (stage % NB) + q: block q of that stage is readable
+  uint32_t fullbits = 0;  // bit stage % NB: every score visible to every real row of the wave
+  uint32_t tailbits = 0;  // bit stage % NB: some key of the stage is past the context or unreadable
   auto issue = [&](int st) {
+    if (2 * st - tbl_base >= 64) {  // uniform, every 32 stages
+      tbl_base += 64;
+      tbl_cur = tbl_nxt;
+      tbl_nxt = tbl_base + 64 + lane < nblk ? bt[tbl_base + 64 + lane] : 0;
+    }
+    const int cur[2] = {__builtin_amdgcn_readlane(tbl_cur, 2 * st - tbl_base),
+                        __builtin_amdgcn_readlane(tbl_cur, 2 * st + 1 - tbl_base)};
     uint32_t ok2 = 0;
-    // consumed at once: no scalar load may stay in flight across the
-    // compute phases, whose LDS waits could then not count partially
-    const int cur[2] = {btc[min(2 * st, nblk - 1)], btc[min(2 * st + 1, nblk - 1)]};
     __amdgpu_buffer_rsrc_t rk[2], rv[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -340,8 +347,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
       rk[q] = tile_rsrc(kpool + off, ok ? kTileU4 * 16 : 0);
       rv[q] = tile_rsrc(vpool + off, ok ? kTileU4 * 16 : 0);
     }
+    const int tok0 = (blk_lo + 2 * st) * kBlock;
+    const bool full = ok2 == 3u && tok0 + 31 < L && tok0 + 31 <= qpos_lo &&
+                      (a.window <= 0 || qpos_hi - tok0 < a.window);
+    const bool tail = !(ok2 == 3u && tok0 + 2 * kBlock <= L);
     const int slot = st & (NB - 1);
     okbits = (okbits & ~(3u << (2 * slot))) | (ok2 << (2 * slot));
+    fullbits = (fullbits & ~(1u << slot)) | ((uint32_t)full << slot);
+    tailbits = (tailbits & ~(1u << slot)) | ((uint32_t)tail << slot);
     u32x4* dst = smem + slot * kStageU4;
     // K runs 2p, 2p+1 form 2 KiB: the first KiB from block 0 (run 2p's lanes
     // n < 16, then run 2p+1's), the second from block 1; each copy reads
@@ -362,20 +375,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
   auto k_run = [](int s) { return (s >> 1) * 2 * kWave + (s & 1) * 32; };
   auto stage_tok0 = [&](int st) { return (blk_lo + 2 * st) * kBlock; };
   auto stage_ok = [&](int st) { return (okbits >> (2 * (st & (NB - 1)))) & 3u; };
-  // every score of the stage is visible to every real row of this wave
-  auto stage_full = [&](int st) {
-    const int tok0 = stage_tok0(st);
-    return stage_ok(st) == 3u && tok0 + 31 < L && tok0 + 31 <= qpos_lo &&
-           (a.window <= 0 || qpos_hi - tok0 < a.window);
-  };
+  auto stage_full = [&](int st) { return (fullbits >> (st & (NB - 1))) & 1u; };
   // Keys past the context (or of an unreadable block) may hold anything; in
   // LDS their V entries are cleared once the stage has landed, so that the
   // products never multiply a zero probability by a non-finite value.  Rare
   // (the context's last block), done by the whole workgroup.
   auto clear_v_tail = [&](int st) {
+    if (!((tailbits >> (st & (NB - 1))) & 1u)) return;
     const int tok0 = stage_tok0(st);
     const uint32_t okk = stage_ok(st);
-    if (okk == 3u && tok0 + 2 * kBlock <= L) return;
     u32x4* vr = smem + (st & (NB - 1)) * kStageU4 + KD * kWave;
     for (int c = threadIdx.x; c < 2 * XT * kWave; c += kThreads) {
       const int q = (c >> 6) & 1, kgc = (c >> 5) & 1;
@@ -471,6 +479,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
     const float m_use = m_run == kNegInf ? 0.f : m_run;
     f32x16 acc = {};
     float p[16];
+    uint32_t pw[8];  // probabilities as bf16 pairs
+    float ls = 0.f;
     {
       u32x4 kf[4];
 #pragma unroll
@@ -481,22 +491,18 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
         acc = mma32_bf16(kf[i & 3], qf[i], acc);
         if (i + 4 < KD) kf[i & 3] = kb[k_run(i + 4)];
 #pragma unroll
-        for (int e = 0; e < kE; ++e) p[i * kE + e] = fast_exp2(sv[i * kE + e] - m_use);
+        for (int e = 0; e < kE; ++e) {
+          const int v = i * kE + e;
+          p[v] = fast_exp2(sv[v] - m_use);
+          ls += p[v];
+          if (v & 1) pw[v >> 1] = pack_bf16x2_hw(p[v - 1], p[v]);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    float ls = 0.f;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) ls += p[v];
     l_run += ls;
-    u32x4 pb[2];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      pb[q] = u32x4{pack_bf16x2_hw(p[8 * q + 0], p[8 * q + 1]), pack_bf16x2_hw(p[8 * q + 2], p[8 * q + 3]),
-                    pack_bf16x2_hw(p[8 * q + 4], p[8 * q + 5]), pack_bf16x2_hw(p[8 * q + 6], p[8 * q + 7])};
-      asm volatile("" ::"v"(pb[q]));  // computed here, not sunk into phase 2
-    }
-    asm volatile("" ::"v"(l_run));
+    const u32x4 pb[2] = {u32x4{pw[0], pw[1], pw[2], pw[3]}, u32x4{pw[4], pw[5], pw[6], pw[7]}};
+    asm volatile("" ::"v"(pb[0]), "v"(pb[1]), "v"(l_run));  // computed here, not sunk into phase 2
 
     mma_result_fence();
     if (!stage_full(k + 1)) mask_scores(k + 1, acc);
