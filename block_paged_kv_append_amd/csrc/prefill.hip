@@ -18,6 +18,13 @@
 #include "attn_tile.hpp"
 #include "launch.hpp"
 
+#ifndef PKV_PREFILL_AHEAD
+#define PKV_PREFILL_AHEAD 4
+#endif
+#ifndef PKV_PREFILL_RING
+#define PKV_PREFILL_RING 4
+#endif
+
 namespace pkv {
 namespace {
 
@@ -253,6 +260,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
   constexpr int kRuns = KD + 2 * XT;            // 1 KiB runs per stage
   constexpr int kStageU4 = kRuns * kWave;       // 16-byte chunks per stage
   constexpr int kDma = kRuns / kWaves;          // copies per wave per stage
+  static_assert(kDma * 2 == 2 * XT, "one copy every second P V product");
+  constexpr int kAhead = PKV_PREFILL_AHEAD;     // LDS operand reads in flight
   constexpr int kTileU4 = D * kBlock * 2 / 16;  // chunks of one block's K (or V) in the pool
   static_assert(KD % kWaves == 0 && (2 * XT) % kWaves == 0, "runs must split over the waves");
   static_assert(NB >= 3 && (NB & (NB - 1)) == 0, "ring of 4 or 8 stages");
@@ -327,7 +336,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
   uint32_t okbits = 0;    // bit 2 * (stage % NB) + q: block q of that stage is readable
   uint32_t fullbits = 0;  // bit stage % NB: every score visible to every real row of the wave
   uint32_t tailbits = 0;  // bit stage % NB: some key of the stage is past the context or unreadable
-  auto issue = [&](int st) {
+  // Copies of one stage: descriptors made once (prepare), the copies issued
+  // one every second product of the next P V phase (copy); in one burst
+  // they would hold the waves on the vector memory path.
+  __amdgpu_buffer_rsrc_t crk0, crk1, crv0, crv1;
+  u32x4* cdst = smem;
+  auto prepare = [&](int st) {
     if (2 * st - tbl_base >= 64) {  // uniform, every 32 stages
       tbl_base += 64;
       tbl_cur = tbl_nxt;
@@ -336,7 +350,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
     const int cur[2] = {__builtin_amdgcn_readlane(tbl_cur, 2 * st - tbl_base),
                         __builtin_amdgcn_readlane(tbl_cur, 2 * st + 1 - tbl_base)};
     uint32_t ok2 = 0;
-    __amdgpu_buffer_rsrc_t rk[2], rv[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
       const int lb = 2 * st + q;
@@ -344,8 +357,15 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
       ok2 |= (uint32_t)ok << q;
       const size_t off = ((size_t)(ok ? cur[q] : 0) * Hkv + g) * kTileU4;
       // an unreadable block gets an empty range: its copies read zeros
-      rk[q] = tile_rsrc(kpool + off, ok ? kTileU4 * 16 : 0);
-      rv[q] = tile_rsrc(vpool + off, ok ? kTileU4 * 16 : 0);
+      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kpool + off, ok ? kTileU4 * 16 : 0);
+      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vpool + off, ok ? kTileU4 * 16 : 0);
+      if (q == 0) {
+        crk0 = rk;
+        crv0 = rv;
+      } else {
+        crk1 = rk;
+        crv1 = rv;
+      }
     }
     const int tok0 = (blk_lo + 2 * st) * kBlock;
     const bool full = ok2 == 3u && tok0 + 31 < L && tok0 + 31 <= qpos_lo &&
@@ -355,20 +375,24 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
     okbits = (okbits & ~(3u << (2 * slot))) | (ok2 << (2 * slot));
     fullbits = (fullbits & ~(1u << slot)) | ((uint32_t)full << slot);
     tailbits = (tailbits & ~(1u << slot)) | ((uint32_t)tail << slot);
-    u32x4* dst = smem + slot * kStageU4;
-    // K runs 2p, 2p+1 form 2 KiB: the first KiB from block 0 (run 2p's lanes
-    // n < 16, then run 2p+1's), the second from block 1; each copy reads
-    // one block
-#pragma unroll
-    for (int e = 0; e < KD / kWaves; ++e) {
-      const int pr = 2 * e + (wave >> 1), blk = wave & 1;
-      copy_to_lds(rk[blk], (64 * pr + k_off) * 16, dst + pr * 2 * kWave + blk * kWave);
+    cdst = smem + slot * kStageU4;
+  };
+  // This wave's copy j of the prepared stage.  K runs 2p, 2p+1 form 2 KiB:
+  // the first KiB from block 0 (run 2p's lanes n < 16, then run 2p+1's),
+  // the second from block 1; each copy reads one block.
+  auto copy = [&](int j) {
+    if (j < KD / kWaves) {
+      const int pr = 2 * j + (wave >> 1);
+      copy_to_lds((wave & 1) ? crk1 : crk0, (64 * pr + k_off) * 16, cdst + pr * 2 * kWave + (wave & 1) * kWave);
+    } else {
+      const int x = 2 * (j - KD / kWaves) + (wave >> 1);
+      copy_to_lds((wave & 1) ? crv1 : crv0, (64 * x + v_off) * 16, cdst + (KD + 2 * x + (wave & 1)) * kWave);
     }
+  };
+  auto issue = [&](int st) {
+    prepare(st);
 #pragma unroll
-    for (int e = 0; e < 2 * XT / kWaves; ++e) {
-      const int x = 2 * e + (wave >> 1);
-      copy_to_lds(rv[wave & 1], (64 * x + v_off) * 16, dst + (KD + 2 * x + (wave & 1)) * kWave);
-    }
+    for (int j = 0; j < kDma; ++j) copy(j);
   };
 
   // chunk offset of K run s within a stage, relative to k_rd
@@ -470,8 +494,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
     wait_vmem<(NB - 3) * kDma>();  // stage k + 1 has landed (this wave's part)
     lds_barrier();                 // ... and every other wave's
     if (k + 1 < nstage) clear_v_tail(k + 1);
-    issue(k + NB - 1);  // into the slot stage k - 1 used
-    if (!wave_live) continue;
+    prepare(k + NB - 1);  // into the slot stage k - 1 used
+    if (!wave_live) {
+#pragma unroll
+      for (int j = 0; j < kDma; ++j) copy(j);
+      continue;
+    }
 
     // phase 1: the order below is the issue order (scheduling barriers)
     constexpr int kE = 16 / KD;  // score elements handled per product
@@ -482,14 +510,14 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
     uint32_t pw[8];  // probabilities as bf16 pairs
     float ls = 0.f;
     {
-      u32x4 kf[4];
+      u32x4 kf[kAhead];
 #pragma unroll
-      for (int i = 0; i < 4 && i < KD; ++i) kf[i] = kb[k_run(i)];
+      for (int i = 0; i < kAhead && i < KD; ++i) kf[i] = kb[k_run(i)];
 #pragma unroll
       for (int i = 0; i < KD; ++i) {
         __builtin_amdgcn_sched_barrier(0);
-        acc = mma32_bf16(kf[i & 3], qf[i], acc);
-        if (i + 4 < KD) kf[i & 3] = kb[k_run(i + 4)];
+        acc = mma32_bf16(kf[i % kAhead], qf[i], acc);
+        if (i + kAhead < KD) kf[i % kAhead] = kb[k_run(i + kAhead)];
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
           const int v = i * kE + e;
@@ -511,16 +539,17 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
     const u32x4* vb = smem + (k & (NB - 1)) * kStageU4 + KD * kWave + lane;
     {
       constexpr int NU = 2 * XT;  // products: u = q * XT + x
-      u32x4 vf[4];
+      u32x4 vf[kAhead];
 #pragma unroll
-      for (int u = 0; u < 4 && u < NU; ++u) vf[u] = vb[(2 * (u % XT) + u / XT) * kWave];
+      for (int u = 0; u < kAhead && u < NU; ++u) vf[u] = vb[(2 * (u % XT) + u / XT) * kWave];
       float mx = kNegInf;
 #pragma unroll
       for (int u = 0; u < NU; ++u) {
         __builtin_amdgcn_sched_barrier(0);
         const int x = u % XT, q = u / XT;
-        o[x] = mma32_bf16(vf[u & 3], pb[q], o[x]);
-        if (u + 4 < NU) vf[u & 3] = vb[(2 * ((u + 4) % XT) + (u + 4) / XT) * kWave];
+        o[x] = mma32_bf16(vf[u % kAhead], pb[q], o[x]);
+        if (u + kAhead < NU) vf[u % kAhead] = vb[(2 * ((u + kAhead) % XT) + (u + kAhead) / XT) * kWave];
+        if ((u & 1) == 0) copy(u >> 1);  // kDma = NU / 2 copies
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
           sv[u * kE + e] = logit(acc[u * kE + e]);
@@ -559,9 +588,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
                 pack_bf16x2_hw(o[x][4 * h + 2] * inv, o[x][4 * h + 3] * inv)};
 }
 
-#ifndef PKV_PREFILL_RING
-#define PKV_PREFILL_RING 4
-#endif
 template <int D>
 void launch_mma32(PrefillArgs a, hipStream_t stream) {
   if (a.softcap > 0.f)
