@@ -46,7 +46,7 @@ def parse_args():
     p = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=200)
-    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--replicas", type=int, default=0, help="pool replicas (0: enough for 1 GiB)")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
@@ -171,6 +171,16 @@ def capture(torch, fn):
     return g
 
 
+def warm(g, torch, seconds=0.4):
+    """Replay ``g`` for about ``seconds``: the GPU's clocks ramp up under
+    load, and a kernel timed from cold runs several percent slow."""
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(8):
+            g.replay()
+        torch.cuda.synchronize()
+
+
 def time_steps(bench, steps, warmup, with_append, torch):
     """One HIP graph holds R consecutive steps, one per pool replica (as an
     engine's captured decode step holds every layer's attention); each step
@@ -186,6 +196,7 @@ def time_steps(bench, steps, warmup, with_append, torch):
     torch.cuda.synchronize()
     g = capture(torch, all_steps)
     reps = max(1, -(-steps // bench.R))
+    warm(g, torch)  # clocks up first, then the W warm-up steps proper
     for _ in range(max(1, -(-warmup // bench.R))):
         g.replay()
     torch.cuda.synchronize()
@@ -209,8 +220,7 @@ def time_decode_op(bench, iters, torch):
     all_decodes()
     torch.cuda.synchronize()
     g = capture(torch, all_decodes)
-    g.replay()
-    torch.cuda.synchronize()
+    warm(g, torch)
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(iters)]
     for i in range(iters):
@@ -219,6 +229,9 @@ def time_decode_op(bench, iters, torch):
         ev[i][1].record()
     torch.cuda.synchronize()
     return float(np.mean([a.elapsed_time(b) for a, b in ev])) / bench.R
+
+
+APPEND_REPEAT = 16  # appends per graph replay: one alone is shorter than a launch
 
 
 def time_prefill(case, iters, warmup, torch, pkv):
@@ -237,8 +250,9 @@ def time_prefill(case, iters, warmup, torch, pkv):
     bt = torch.from_numpy(case.block_tables).cuda()
     cl = torch.from_numpy(case.context_lens).cuda()
 
-    def append():
-        pkv.paged_kv_append(k_new, v_new, slots, kp, vp)
+    def append():  # the same rows again: idempotent, and enough work per replay
+        for _ in range(APPEND_REPEAT):
+            pkv.paged_kv_append(k_new, v_new, slots, kp, vp)
 
     def prefill():
         pkv.paged_attn_prefill(out, q, cu, case.max_q_len, kp, vp, bt, cl, case.max_context_len,
@@ -252,7 +266,7 @@ def time_prefill(case, iters, warmup, torch, pkv):
     for g in (ga, gp):
         for _ in range(warmup):
             g.replay()
-        torch.cuda.synchronize()
+        warm(g, torch)
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(iters)]
         for i in range(iters):
@@ -261,7 +275,7 @@ def time_prefill(case, iters, warmup, torch, pkv):
             ev[i][1].record()
         torch.cuda.synchronize()
         res.append(float(np.mean([a.elapsed_time(b) for a, b in ev])))
-    return res[0], res[1]
+    return res[0] / APPEND_REPEAT, res[1]
 
 
 def calibrate_copy(torch):
