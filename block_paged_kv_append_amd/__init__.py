@@ -164,15 +164,16 @@ _ws_lock = threading.Lock()
 
 
 def decode_workspace(nbytes: int, device, stream=None):
-    """A scratch workspace of at least ``nbytes``, cached per device and stream
-    (calls on one stream run in order, so they can share it)."""
+    """A zero-filled workspace of at least ``nbytes``, cached per device and
+    stream (calls on one stream run in order, so they can share it; each call
+    leaves its counters at zero again)."""
     import torch
 
     key = (str(device), _stream(stream))
     with _ws_lock:
         ws = _ws_cache.get(key)
         if ws is None or ws.numel() < nbytes:
-            ws = torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+            ws = torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
             _ws_cache[key] = ws
         return ws
 

@@ -28,6 +28,12 @@ HIPCC_FLAGS = [
 ]
 
 
+# per-source flags.  decode: the matrix-core accumulators stay in the vector
+# file, where the (rare) rescale multiplies them; in the accumulator file
+# the compiler copies them across and back on every block.
+SOURCE_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def hipcc() -> str:
     path = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
     if not os.path.exists(path):
@@ -38,7 +44,7 @@ def hipcc() -> str:
 def _compile(src: str, extra) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj, "-I", INCLUDE,
-           "-I", CSRC] + HIPCC_FLAGS + list(extra)
+           "-I", CSRC] + HIPCC_FLAGS + SOURCE_FLAGS.get(src, []) + list(extra)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

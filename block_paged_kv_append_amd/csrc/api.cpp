@@ -121,6 +121,9 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
     return fail(PKV_EUNSUPPORTED, "%s: partition_size %d is not a multiple of 16", fn,
                 partition_size);
   if (num_seqs == 0) return PKV_OK;
+  if ((long long)num_seqs * num_kv_heads > pkv::kMaxSegments)
+    return fail(PKV_EUNSUPPORTED, "%s: num_seqs * num_kv_heads = %lld exceeds %d", fn,
+                (long long)num_seqs * num_kv_heads, pkv::kMaxSegments);
   const size_t need = pkv::decode_workspace_bytes(num_seqs, num_kv_heads, gqa_group, head_dim,
                                                   max_context_len, partition_size);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
@@ -147,7 +150,11 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
 
   const size_t slots =
       pkv::decode_num_slots(num_seqs, num_kv_heads, max_context_len, partition_size);
+  // counters first, at a fixed offset and capacity: whatever sizes a call
+  // uses, no other call's data ever lands on them
   char* base = static_cast<char*>(workspace);
+  a.seg_count = reinterpret_cast<int32_t*>(base);
+  base += pkv::kCounterBytes;
   a.part_o = reinterpret_cast<float*>(base);
   base += align256(slots * gqa_group * head_dim * sizeof(float));
   a.part_ml = reinterpret_cast<float*>(base);
@@ -186,7 +193,7 @@ size_t decode_num_slots(int32_t num_seqs, int32_t num_kv_heads, int32_t max_cont
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
                               int32_t head_dim, int32_t max_context_len, int32_t partition_size) {
   const size_t slots = decode_num_slots(num_seqs, num_kv_heads, max_context_len, partition_size);
-  return align256(slots * gqa_group * head_dim * sizeof(float)) +
+  return kCounterBytes + align256(slots * gqa_group * head_dim * sizeof(float)) +
          align256(slots * gqa_group * 2 * sizeof(float));
 }
 

