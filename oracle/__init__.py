@@ -9,9 +9,11 @@ from .paged_attention import (  # noqa: F401
     append,
     attend,
     decode,
+    decode_append,
     decode_splitk,
     gather_sequence,
     merge_partials,
+    new_token_slots,
     prefill,
     scores,
     values,

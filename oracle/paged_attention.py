@@ -296,3 +296,33 @@ def append(k_new, v_new, slot_mapping, k_pool, v_pool, dtype="bf16"):
         kp[blk, :, :, off, :] = k_new[i].reshape(Hkv, D // X, X)
         vp[blk, :, :, off] = v_new[i]
     return kp, vp
+
+
+# ---------------------------------------------------------------------------
+# [flow] one decode tick: append every sequence's newest token, then decode
+# ---------------------------------------------------------------------------
+def new_token_slots(block_tables, context_lens):
+    """Slot of each sequence's newest token: position ``L_b - 1`` (``L_b``
+    counts it) lives in block ``block_tables[b][(L_b-1) // 16]`` at offset
+    ``(L_b-1) % 16`` ([engine]: tokens are found through the block table);
+    ``-1`` (nothing to append) when ``L_b == 0``."""
+    slots = np.full(len(context_lens), -1, dtype=np.int64)
+    for b, L in enumerate(np.asarray(context_lens).tolist()):
+        if L > 0:
+            slots[b] = int(block_tables[b][(L - 1) // BLOCK]) * BLOCK + (L - 1) % BLOCK
+    return slots
+
+
+def decode_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, scale,
+                  softcap=0.0, window=0, dtype="bf16"):
+    """A decode tick as [flow] describes it: each active request's newest
+    token (rows ``k_new/v_new [B, Hkv, D]``) is appended to the pool, then one
+    batched decode attends over every cached token including it.  Exactly
+    :func:`append` at :func:`new_token_slots` followed by :func:`decode`.
+
+    Returns ``out``, ``lse`` and the updated pools' bits."""
+    kp, vp = append(k_new, v_new, new_token_slots(block_tables, context_lens), k_pool, v_pool,
+                    dtype)
+    out, lse = decode(q, kp, vp, block_tables, context_lens, scale, softcap, window, dtype)
+    return out, lse, kp, vp
+

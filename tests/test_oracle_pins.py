@@ -455,6 +455,57 @@ def test_p10_append_round_trip(dtype):
     np.testing.assert_array_equal(V[cached:], f32vals(case.v_new[n0:n0 + 17, 1], dtype))
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("L,window,softcap", [(1, 0, 0.0), (16, 0, 2.0), (17, 0, 0.0),
+                                               (33, 8, 0.0), (40, 0, 3.0)])
+def test_p13_decode_tick_equals_dense_attention_with_the_new_row(dtype, L, window, softcap):
+    """A decode tick (append the newest token, then decode) equals textbook
+    attention over the cached rows followed by the new row; the pool's slot
+    for that token held NaN beforehand and holds exactly the new row after."""
+    rng = np.random.default_rng(1300 + L)
+    Hkv, G, D = 2, 2, 16
+    K = rand_f32(rng, (Hkv, L, D), dtype)
+    V = rand_f32(rng, (Hkv, L, D), dtype)
+    q = rand_f32(rng, (1, Hkv * G, D), dtype)
+    nblk = (L + BS - 1) // BS
+    table = rng.permutation(nblk + 3)[:nblk].astype(np.int32)
+    kp, vp, _ = scatter_contiguous(K, V, dtype, num_blocks=nblk + 3, table=table)
+    X = 16 // wl.elem_bytes(dtype)
+    blk, off = int(table[(L - 1) // BS]), (L - 1) % BS
+    kp[blk, :, :, off, :] = wl.nan_bits(dtype)  # the new token is not in the pool yet
+    vp[blk, :, :, off] = wl.nan_bits(dtype)
+    k_new = wl.to_bits(K[:, L - 1][None], dtype)  # [1, Hkv, D]
+    v_new = wl.to_bits(V[:, L - 1][None], dtype)
+    scale = 0.37
+    out, lse, kp2, vp2 = oracle.decode_append(wl.to_bits(q, dtype), k_new, v_new, kp, vp,
+                                              table[None], np.array([L]), scale, softcap,
+                                              window, dtype)
+    for g in range(Hkv):
+        for d in range(D):
+            assert kp2[blk, g, d // X, off, d % X] == k_new[0, g, d]
+            assert vp2[blk, g, d, off] == v_new[0, g, d]
+    changed_k = np.argwhere(kp2.view(np.uint8) != kp.view(np.uint8))
+    assert all(int(i[0]) == blk for i in changed_k)
+    for h in range(Hkv * G):
+        g = h // G
+        keep = (lambda t: L - 1 - t < window) if window > 0 else (lambda t: True)
+        ref, ref_lse = textbook(q[0, h], K[g], V[g], scale, softcap, keep)
+        np.testing.assert_allclose(out[0, h], ref, rtol=1e-12, atol=1e-12)
+        assert abs(lse[0, h] - ref_lse) < 1e-12
+    assert oracle.new_token_slots(table[None], np.array([L]))[0] == blk * BS + off
+
+
+def test_p13_decode_tick_skips_empty_sequences():
+    case = wl.make_decode_case(1310, [0, 5], 2, 1, 16, "f32")
+    slots = oracle.new_token_slots(case.block_tables, case.context_lens)
+    assert slots[0] == -1 and slots[1] == int(case.block_tables[1, 0]) * BS + 4
+    k_new = np.zeros((2, 1, 16), dtype=np.uint32)
+    out, lse, kp, vp = oracle.decode_append(case.q, k_new, k_new, case.k_pool, case.v_pool,
+                                            case.block_tables, case.context_lens, case.scale,
+                                            dtype="f32")
+    assert (out[0] == 0).all() and np.isneginf(lse[0]).all()
+
+
 def test_p10_append_rejects_bad_slots():
     case = wl.make_prefill_case(102, [3], [4], 2, 1, 16, "bf16")
     dup = case.slot_mapping.copy()
