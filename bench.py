@@ -98,6 +98,13 @@ def append_bytes(num_tokens, Hkv, D, s) -> int:
     return 2 * (2 * num_tokens * Hkv * D * s) + 4 * num_tokens
 
 
+def tick_bytes(case) -> int:
+    """A fused decode tick: the decode's bytes, plus the new K and V rows read
+    and written into the pool."""
+    s = 2 if case.dtype == "bf16" else 4
+    return decode_bytes(case) + 2 * (2 * case.num_seqs * case.num_kv_heads * case.head_dim * s)
+
+
 def prefill_flops(case) -> float:
     pairs = 0
     for b in range(case.num_seqs):
@@ -162,6 +169,17 @@ class DecodeBench:
     def append(self, r):
         self.pkv.paged_kv_append(self.k_new, self.v_new, self.slots[r], self.kp, self.vp)
 
+    def tick(self, r):
+        """The fused form: append and decode in one launch."""
+        c, pkv = self.case, self.pkv
+        pkv.paged_attn_decode_append(self.out, self.q, self.k_new, self.v_new, self.kp, self.vp,
+                                     self.bt[r], self.cl, c.max_context_len, c.scale, c.softcap,
+                                     c.window, partition_size=c.partition_size, workspace=self.ws)
+
+    def two_calls(self, r):
+        self.append(r)
+        self.decode(r)
+
 
 def capture(torch, fn):
     """A HIP graph of whatever ``fn`` launches on the current stream."""
@@ -181,16 +199,14 @@ def warm(g, torch, seconds=0.4):
         torch.cuda.synchronize()
 
 
-def time_steps(bench, steps, warmup, with_append, torch):
+def time_steps(bench, steps, warmup, step, torch):
     """One HIP graph holds R consecutive steps, one per pool replica (as an
     engine's captured decode step holds every layer's attention); each step
-    appends the tick's new rows, then decodes.  Returns the wall time of
+    is ``step(r)``: the tick's append and decode.  Returns the wall time of
     ``steps`` steps (``steps / R`` replays, rounded up to whole replays)."""
     def all_steps():
         for r in range(bench.R):
-            if with_append:
-                bench.append(r)
-            bench.decode(r)
+            step(r)
 
     all_steps()  # eager warm-up
     torch.cuda.synchronize()
@@ -207,15 +223,17 @@ def time_steps(bench, steps, warmup, with_append, torch):
     return (time.perf_counter() - t0) * steps / (reps * bench.R)
 
 
-def time_decode_op(bench, iters, torch):
-    """Average duration of one decode operation: a graph of R decode calls
-    (one per replica) replayed ``iters`` times, each replay bracketed by HIP
-    events on the stream, divided by R."""
+def time_decode_op(bench, iters, torch, op=None):
+    """Average duration of one decode operation (``op(r)``, by default the
+    plain decode): a graph of R calls (one per replica) replayed ``iters``
+    times, each replay bracketed by HIP events on the stream, divided by R."""
     import numpy as np
+
+    op = op or bench.decode
 
     def all_decodes():
         for r in range(bench.R):
-            bench.decode(r)
+            op(r)
 
     all_decodes()
     torch.cuda.synchronize()
@@ -347,13 +365,12 @@ def main():
     print(f"# setup {time.perf_counter() - t_setup:.1f}s, pool replicas {bench.R}", file=sys.stderr,
           flush=True)
 
-    wall = time_steps(bench, args.steps, args.warmup, True, torch)
+    wall = time_steps(bench, args.steps, args.warmup, bench.tick, torch)
     ms_per_step = wall * 1e3 / args.steps
-    dbytes = decode_bytes(case)
-    abytes = append_bytes(case.num_seqs, case.num_kv_heads, case.head_dim, 2)
-    value = (dbytes + abytes) / (ms_per_step * 1e-3) / 1e9
-    kern_avg_ms = time_decode_op(bench, max(10, args.steps // bench.R), torch)
-    achieved = dbytes / (kern_avg_ms * 1e-3) / 1e9
+    tbytes = tick_bytes(case)
+    value = tbytes / (ms_per_step * 1e-3) / 1e9
+    kern_avg_ms = time_decode_op(bench, max(10, args.steps // bench.R), torch, bench.tick)
+    achieved = tbytes / (kern_avg_ms * 1e-3) / 1e9
     traffic = measured_traffic("decode")
     line = {
         "metric": METRIC,
@@ -369,7 +386,8 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": "gemma_decode: 32 seqs, ctx U[512,4096], 8q/2kv heads, D256, bf16, "
-                               "softcap 50, block 16; step = append 32 tokens + paged decode",
+                               "softcap 50, block 16; step = one decode tick: the 32 new "
+                               "tokens appended and decoded in one launch",
                    "num_seqs": case.num_seqs, "context_tokens": int(case.context_lens.sum()),
                    "pool_replicas": bench.R},
         "tok_per_s": round(case.num_seqs / (ms_per_step * 1e-3), 1),
@@ -377,11 +395,19 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "paged_attn_decode: decode_kernel (balanced split) + merge_kernel",
-                     "kernel_ms": round(kern_avg_ms, 5), "algorithmic_bytes": dbytes},
+                     "kernel": "paged_attn_decode_append: decode_kernel (balanced split, "
+                               "fused append, in-launch merge)",
+                     "kernel_ms": round(kern_avg_ms, 5), "algorithmic_bytes": tbytes},
     }
 
     if not args.quick:
+        # the same tick as two launches (append, then decode), and the decode alone
+        two_ms = time_steps(bench, args.steps, args.warmup, bench.two_calls, torch) * 1e3 / args.steps
+        dec_ms = time_decode_op(bench, max(10, args.steps // bench.R), torch)
+        line["step_forms"] = {"fused_ms": round(ms_per_step, 5),
+                              "append_then_decode_ms": round(two_ms, 5),
+                              "decode_only_ms": round(dec_ms, 5),
+                              "decode_only_gbs": round(decode_bytes(case) / (dec_ms * 1e-3) / 1e9, 1)}
         extra = {}
         pc = wl.chunked_prefill_shared_prefix()
         app_ms, pre_ms = time_prefill(pc, 20, 3, torch, pkv)

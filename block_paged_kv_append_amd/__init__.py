@@ -37,8 +37,16 @@ SIGNATURES = {
                                          _I, _F, _F, _I, _P, _Z, _I, _P]),
     "paged_attn_decode_splitk": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I,
                                                 _I, _I, _I, _F, _F, _I, _I, _P, _Z, _I, _P]),
+    "paged_attn_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I,
+                                                _I, _I, _I, _I, _I, _F, _F, _I, _I, _P, _Z, _I,
+                                                _P]),
     "paged_attn_prefill": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I,
                                           _I, _I, _I, _I, _F, _F, _I, _I, _P]),
+    "pkv_decode_graph_create": (ctypes.c_int, [ctypes.POINTER(_P), _P, _P, _P, _P, _P, _P, _P,
+                                               _I, _P, _I, _P, _I, _I, _I, _I, _I, _I, _F, _F,
+                                               _I, _I, _I]),
+    "pkv_decode_graph_launch": (ctypes.c_int, [_P, _P]),
+    "pkv_decode_graph_destroy": (None, [_P]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
 
@@ -222,6 +230,80 @@ def paged_attn_decode_splitk(out, q, k_pool, v_pool, block_tables, context_lens,
                                       ws.numel() * ws.element_size(), _dtype_code(q),
                                       _stream(stream))
     _check("paged_attn_decode_splitk", rc)
+
+
+def paged_attn_decode_append(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
+                             max_context_len, scale, softcap=0.0, window=0, partition_size=0,
+                             lse=None, workspace=None, stream=None) -> None:
+    """One decode tick in one launch: rows ``k_new/v_new [B, Hkv, D]`` go to
+    position ``L_b - 1`` of each sequence (through its block table) and the
+    decode attends to them; ``partition_size > 0`` selects the split-K form."""
+    nb, hkv, d, B, G, MB = _decode_dims(out, q, k_pool, v_pool, block_tables, context_lens)
+    if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
+        raise ValueError("k_new/v_new must be [num_seqs, num_kv_heads, head_dim]")
+    if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+        raise TypeError("k_new/v_new dtype must match the pools")
+    need = paged_attn_decode_workspace_size(B, hkv, G, d, max_context_len, partition_size)
+    ws = workspace if workspace is not None else decode_workspace(need, q.device, stream)
+    lib = load_library()
+    rc = lib.paged_attn_decode_append(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                      _ptr(k_pool), _ptr(v_pool), nb,
+                                      _i32(block_tables, "block_tables"), MB,
+                                      _i32(context_lens, "context_lens"), int(max_context_len), B,
+                                      hkv, G, d, BLOCK_SIZE, float(scale), float(softcap),
+                                      int(window), int(partition_size), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _dtype_code(q),
+                                      _stream(stream))
+    _check("paged_attn_decode_append", rc)
+
+
+def decode_bucket(num_seqs: int) -> int:
+    """The batch-size bucket a tick of ``num_seqs`` sequences replays: the
+    next power of two."""
+    n = 1
+    while n < num_seqs:
+        n *= 2
+    return n
+
+
+class DecodeGraph:
+    """A decode tick (``paged_attn_decode_append``) captured once for a bucket
+    of ``q.shape[0]`` rows (``pkv_decode_graph`` in include/pkv.h).  The
+    tensors passed here are bound into the graph: write each tick's q, new
+    rows, tables and lengths into them (unused rows: length 0), then call
+    :meth:`launch`.  The graph owns its workspace."""
+
+    def __init__(self, out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,
+                 max_context_len, scale, softcap=0.0, window=0, partition_size=0, lse=None):
+        nb, hkv, d, B, G, MB = _decode_dims(out, q, k_pool, v_pool, block_tables, context_lens)
+        if tuple(k_new.shape) != (B, hkv, d) or tuple(v_new.shape) != (B, hkv, d):
+            raise ValueError("k_new/v_new must be [num_seqs, num_kv_heads, head_dim]")
+        if k_new.dtype != k_pool.dtype or v_new.dtype != k_pool.dtype:
+            raise TypeError("k_new/v_new dtype must match the pools")
+        self._lib = load_library()
+        self._bound = (out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, lse)
+        h = ctypes.c_void_p()
+        rc = self._lib.pkv_decode_graph_create(
+            ctypes.byref(h), _ptr(out), _ptr(lse), _ptr(q), _ptr(k_new), _ptr(v_new),
+            _ptr(k_pool), _ptr(v_pool), nb, _i32(block_tables, "block_tables"), MB,
+            _i32(context_lens, "context_lens"), int(max_context_len), B, hkv, G, d, BLOCK_SIZE,
+            float(scale), float(softcap), int(window), int(partition_size), _dtype_code(q))
+        _check("pkv_decode_graph_create", rc)
+        self._h = h
+
+    def launch(self, stream=None) -> None:
+        if self._h is None:
+            raise RuntimeError("DecodeGraph is closed")
+        _check("pkv_decode_graph_launch", self._lib.pkv_decode_graph_launch(self._h,
+                                                                           _stream(stream)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            self._lib.pkv_decode_graph_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
 
 
 def paged_attn_prefill(out, q, cu_q_lens, max_q_len, k_pool, v_pool, block_tables, context_lens,

@@ -106,8 +106,8 @@ long long max_units_per_seq(int32_t max_context_len, int32_t window) {
   return n;
 }
 
-int decode_impl(const char* fn, void* out, float* lse, const void* q, const void* k_pool,
-                const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
+int decode_impl(const char* fn, void* out, float* lse, const void* q, const void* k_new,
+                const void* v_new, const void* k_pool, const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
                 int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
                 int32_t block_size, float scale, float softcap, int32_t window,
@@ -117,6 +117,8 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
                         max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
                         gqa_group, head_dim, block_size, scale, softcap, dtype);
   if (rc != PKV_OK) return rc;
+  if ((k_new == nullptr) != (v_new == nullptr))
+    return fail(PKV_EINVAL, "%s: k_new and v_new must both be given", fn);
   if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0)
     return fail(PKV_EUNSUPPORTED, "%s: partition_size %d is not a multiple of 16", fn,
                 partition_size);
@@ -136,6 +138,8 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
+  a.k_new = k_new;
+  a.v_new = v_new;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.num_blocks = num_blocks;
@@ -197,6 +201,14 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t gq
          align256(slots * gqa_group * 2 * sizeof(float));
 }
 
+int record_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
 }  // namespace pkv
 
 extern "C" {
@@ -248,7 +260,8 @@ int paged_attn_decode(void* out, float* lse, const void* q, const void* k_pool,
                       int32_t gqa_group, int32_t head_dim, int32_t block_size, float scale,
                       float softcap, int32_t window, void* workspace, size_t workspace_bytes,
                       int32_t dtype, struct ihipStream_t* stream) {
-  return decode_impl("paged_attn_decode", out, lse, q, k_pool, v_pool, num_blocks, block_tables,
+  return decode_impl("paged_attn_decode", out, lse, q, nullptr, nullptr, k_pool, v_pool,
+                     num_blocks, block_tables,
                      max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
                      gqa_group, head_dim, block_size, scale, softcap, window, 0, workspace,
                      workspace_bytes, dtype, reinterpret_cast<hipStream_t>(stream));
@@ -265,11 +278,31 @@ int paged_attn_decode_splitk(void* out, float* lse, const void* q, const void* k
   if (partition_size <= 0 || partition_size % PKV_BLOCK_SIZE != 0)
     return fail(PKV_EUNSUPPORTED, "paged_attn_decode_splitk: partition_size %d is not a positive "
                 "multiple of 16", partition_size);
-  return decode_impl("paged_attn_decode_splitk", out, lse, q, k_pool, v_pool, num_blocks,
+  return decode_impl("paged_attn_decode_splitk", out, lse, q, nullptr, nullptr, k_pool, v_pool,
+                     num_blocks,
                      block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
                      num_kv_heads, gqa_group, head_dim, block_size, scale, softcap, window,
                      partition_size, workspace, workspace_bytes, dtype,
                      reinterpret_cast<hipStream_t>(stream));
+}
+
+int paged_attn_decode_append(void* out, float* lse, const void* q, const void* k_new,
+                             const void* v_new, void* k_pool, void* v_pool, int32_t num_blocks,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t max_context_len,
+                             int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                             int32_t head_dim, int32_t block_size, float scale, float softcap,
+                             int32_t window, int32_t partition_size, void* workspace,
+                             size_t workspace_bytes, int32_t dtype, struct ihipStream_t* stream) {
+  const char* fn = "paged_attn_decode_append";
+  if (k_new == nullptr || v_new == nullptr)
+    return fail(PKV_EINVAL, "%s: k_new and v_new are required", fn);
+  if (num_seqs > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16)))
+    return fail(PKV_EINVAL, "%s: k_new / v_new must be 16-byte aligned", fn);
+  return decode_impl(fn, out, lse, q, k_new, v_new, k_pool, v_pool, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
+                     gqa_group, head_dim, block_size, scale, softcap, window, partition_size,
+                     workspace, workspace_bytes, dtype, reinterpret_cast<hipStream_t>(stream));
 }
 
 int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q_lens,

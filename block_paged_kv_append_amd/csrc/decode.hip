@@ -18,19 +18,24 @@
 // inside one segment is a "piece".  Its four waves share the piece's blocks
 // round-robin, each with its own online softmax, and combine through LDS.  A
 // piece that is a whole segment writes the output directly; otherwise it
-// stores (max, sum, unnormalised output) to the workspace.  A second, small
-// kernel then merges the pieces of every split segment by log-sum-exp.  The
-// kernel boundary is what makes the partials visible to the merge: a merge
-// inside the same launch would need device-scope release/acquire fences, and
-// on a multi-XCD part each of those writes back and invalidates an XCD's whole
-// L2, which serialises and costs more than the extra launch.
+// stores (max, sum, unnormalised output) to the workspace and counts itself
+// in on the segment's counter, and the workgroup that counts the last piece
+// merges them all by log-sum-exp in the same launch.  The partials pass
+// between workgroups through device-scope stores and loads, which need no
+// cache writeback or invalidation on a multi-XCD part.
 //
-// Inner loop per wave: double-buffered block loads (K and V fragments for
-// the next block are in flight while the current block is computed), S^T =
-// K Q^T on the matrix cores with the GQA group's query heads as the 16
-// columns (padded with zero rows), mask by select, online softmax in base 2
-// with cross-lane max over the 4 lanes that share a head, then P V on the
-// matrix cores.
+// Fused append (paged_attn_decode_append): the wave that computes a
+// segment's last block takes the newest token's K and V rows from the
+// caller's arrays and also writes them to the pool, so one launch does the
+// tick's append and its decode.
+//
+// Inner loop per wave (bf16): S^T = K Q^T on the matrix cores with the GQA
+// group's query heads as the 16 columns (zero past the group), mask by
+// select, online softmax in base 2 with the row reductions across the four
+// lanes that share a head, then O^T += V^T P^T on the matrix cores.  Blocks
+// stream through registers (one block in flight per wave, two workgroups per
+// CU) or, at head_dim 256, through per-wave LDS rings filled by direct
+// buffer-to-LDS copies.
 #include <algorithm>
 #include <type_traits>
 
@@ -73,6 +78,128 @@ struct Piece {
   int j0, j1;     // blocks [j0, j1) of the segment's visible blocks
   int slot;       // workspace slot if partial
   long long S;    // flattened index of the segment's first unit (balanced mode)
+};
+
+// Fused append (paged_attn_decode_append).  Sequence b's newest token sits
+// at position L - 1, in the segment's last visible block; its K and V rows
+// come from k_new / v_new [b, g] rather than from the pool.  The wave whose
+// blocks include that last block substitutes the rows into its block
+// fragments (lanes hold them in the fragments' own layout, loaded when the
+// piece starts) and writes them to the pool slot; nothing else in the launch
+// reads that block of this kv head, so no ordering with other waves is
+// needed.  ESZ is the element size in bytes, E = 16 / ESZ elements per lane
+// chunk:
+//   K: lane (c, j) holds dims E (4 s + j) .. + E - 1 for every step s
+//      (what a lane serving token c reads of a block's K tile)
+//   V: lane (c, j) holds dim 16 x + c for every output tile x
+template <int ESZ, int D>
+struct NewToken {
+  static constexpr int E = 16 / ESZ;
+  static constexpr int KS = D / (4 * E);      // 16-byte K chunks per lane
+  static constexpr int XT = D / 16;           // V elements per lane
+  static constexpr int VW = (XT * ESZ) / 4;   // ... in 32-bit words
+  u32x4 k[KS];
+  uint32_t v[VW];
+  bool own = false;  // uniform: this wave computes the segment's last block
+  int tn = 0;        // the token's offset within its block
+  char* kt = nullptr;  // the block's K and V tiles (kv head g) in the pool
+  char* vt = nullptr;
+
+  // wave `wave` walks blocks j0 + wave + 4 i, i < nw, of the piece [j0, j1)
+  __device__ __forceinline__ void setup(const DecodeArgs& a, int b, int g, const SeqSpan& sp, int j0,
+                                        int j1, int wave, int nw, int lane) {
+    const int last = sp.nb - 1;
+    own = j1 == sp.nb && nw > 0 && j0 + wave + kWaves * (nw - 1) == last;
+    if (!own) return;
+    const int phys = a.block_tables[(size_t)b * a.max_blocks_per_seq + sp.first_blk + last];
+    if ((unsigned)phys >= (unsigned)a.num_blocks) {  // an unreadable block: nothing to write
+      own = false;
+      return;
+    }
+    const int Hkv = a.num_kv_heads;
+    tn = (sp.L - 1) & (kBlock - 1);
+    const size_t tile = ((size_t)phys * Hkv + g) * D * kBlock * ESZ;
+    kt = reinterpret_cast<char*>(const_cast<void*>(a.k_pool)) + tile;
+    vt = reinterpret_cast<char*>(const_cast<void*>(a.v_pool)) + tile;
+    const size_t row = ((size_t)b * Hkv + g) * D * ESZ;
+    const char* krow = reinterpret_cast<const char*>(a.k_new) + row;
+    const char* vrow = reinterpret_cast<const char*>(a.v_new) + row;
+    const int c = lane & 15, j = lane >> 4;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) k[s] = *reinterpret_cast<const u32x4*>(krow + E * (4 * s + j) * ESZ);
+    if constexpr (ESZ == 2) {
+      const uint16_t* vr = reinterpret_cast<const uint16_t*>(vrow);
+#pragma unroll
+      for (int w = 0; w < VW; ++w)
+        v[w] = (uint32_t)vr[32 * w + c] | ((uint32_t)vr[32 * w + 16 + c] << 16);
+    } else {
+      const uint32_t* vr = reinterpret_cast<const uint32_t*>(vrow);
+#pragma unroll
+      for (int x = 0; x < XT; ++x) v[x] = vr[16 * x + c];
+    }
+  }
+  // raw bits of V dim 16 x + c
+  __device__ __forceinline__ uint32_t vbits(int x) const {
+    if constexpr (ESZ == 2)
+      return (v[x >> 1] >> (16 * (x & 1))) & 0xFFFFu;
+    else
+      return v[x];
+  }
+  // K fragments: lanes of token tn take the new row
+  template <typename V4>
+  __device__ __forceinline__ void put_k(V4 (&kf)[KS], int lane) const {
+    if ((lane & 15) == tn) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s) kf[s] = __builtin_bit_cast(V4, k[s]);
+    }
+  }
+  // bf16 V fragments (tokens 4 j .. 4 j + 3 of dim 16 x + c, 16 bits each)
+  __device__ __forceinline__ void put_v(u32x2 (&vf)[XT], int lane) const {
+    if ((lane >> 4) == (tn >> 2)) {
+      const int e = tn & 3, sh = 16 * (e & 1);
+#pragma unroll
+      for (int x = 0; x < XT; ++x) {
+        const uint32_t keep = ~(0xFFFFu << sh), put = vbits(x) << sh;
+        if (e < 2)
+          vf[x].x = (vf[x].x & keep) | put;
+        else
+          vf[x].y = (vf[x].y & keep) | put;
+      }
+    }
+  }
+  // fp32 V fragments (tokens 4 j .. 4 j + 3 of dim 16 x + c)
+  __device__ __forceinline__ void put_v(f32x4 (&vf)[XT], int lane) const {
+    if ((lane >> 4) == (tn >> 2)) {
+      const int e = tn & 3;
+#pragma unroll
+      for (int x = 0; x < XT; ++x) {
+        const float nv = __builtin_bit_cast(float, vbits(x));
+        vf[x].x = e == 0 ? nv : vf[x].x;
+        vf[x].y = e == 1 ? nv : vf[x].y;
+        vf[x].z = e == 2 ? nv : vf[x].z;
+        vf[x].w = e == 3 ? nv : vf[x].w;
+      }
+    }
+  }
+  // the append itself: the rows into slot tn of the block
+  __device__ __forceinline__ void store(int lane) const {
+    const int c = lane & 15, j = lane >> 4;
+    if (c == tn) {
+#pragma unroll
+      for (int s = 0; s < KS; ++s)
+        *reinterpret_cast<u32x4*>(kt + ((4 * s + j) * kBlock + tn) * 16) = k[s];
+    }
+    if (j == (tn >> 2)) {  // 16 lanes, one per c
+#pragma unroll
+      for (int x = 0; x < XT; ++x) {
+        char* dst = vt + ((size_t)(16 * x + c) * kBlock + tn) * ESZ;
+        if constexpr (ESZ == 2)
+          *reinterpret_cast<uint16_t*>(dst) = (uint16_t)vbits(x);
+        else
+          *reinterpret_cast<uint32_t*>(dst) = vbits(x);
+      }
+    }
+  }
 };
 
 template <bool BF16, int D>
@@ -173,7 +300,12 @@ struct SplitSlots {  // fixed partitions p_lo .. p_hi of one segment
   }
 };
 
-struct BalancedSlots {  // workgroups whose ranges meet [S, E)
+// Workgroups whose ranges meet [S, E).  With W > N every range holds at
+// least one unit, so they are w_first .. w_last.  With W <= N a range holds
+// one unit or none, and the workgroups with an empty range (which store
+// nothing and never count in) lie between those; the pieces are then the
+// owners of units S .. E - 1, one each.
+struct BalancedSlots {
   long long W, S, E;
   int N, w_first, w_last;
   __device__ BalancedSlots(long long W_, long long S_, long long E_, int N_)
@@ -181,12 +313,12 @@ struct BalancedSlots {  // workgroups whose ranges meet [S, E)
     w_first = (int)(((S + 1) * N - 1) / W);
     w_last = (int)((E * N - 1) / W);
   }
-  __device__ int count() const { return w_last - w_first + 1; }
+  __device__ int count() const { return W <= N ? (int)(E - S) : w_last - w_first + 1; }
   __device__ bool slot(int k, int& s) const {
-    const int w = w_first + k;
-    const long long a0 = (long long)w * W / N, a1 = (long long)(w + 1) * W / N;
+    const int w = W <= N ? (int)(((S + k + 1) * N - 1) / W) : w_first + k;
+    const long long a0 = (long long)w * W / N;
     s = a0 < S ? 2 * w + 1 : 2 * w;
-    return a0 < a1;  // an empty range wrote nothing
+    return true;
   }
 };
 
@@ -233,7 +365,7 @@ __device__ void combine_waves(const DecodeArgs& a, const Piece& pc, const float*
 }
 
 // One piece: all four waves of the workgroup.
-template <bool BF16, int D>
+template <bool BF16, int D, bool FUSE>
 __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece& pc, float* lds) {
   using T = typename Elem<BF16>::T;
   using KV = KVFrag<BF16, D>;
@@ -268,6 +400,8 @@ __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece
   const int span = pc.j1 - pc.j0 - wave;
   const int nw = span > 0 ? (span + kWaves - 1) / kWaves : 0;
   int tbl = 0;
+  NewToken<sizeof(T), D> nt;
+  if constexpr (FUSE) nt.setup(a, b, g, sp, pc.j0, pc.j1, wave, nw, lane);
 
   // One K and one V register set.  K of block i + 1 is loaded as soon as the
   // score product of block i has consumed K, V of block i + 1 as soon as the
@@ -292,6 +426,13 @@ __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece
   auto body = [&](int i, auto prefetch) {
     constexpr bool PF = decltype(prefetch)::value;
     const int tok0 = (sp.first_blk + pc.j0 + wave + kWaves * i) * kBlock;
+    if constexpr (FUSE) {
+      if (nt.own && i == nw - 1) {
+        nt.put_k(buf.k, lane);
+        nt.put_v(buf.v, lane);
+        nt.store(lane);
+      }
+    }
     const f32x4 sc = qk_tile<D>(buf, qf);
     bool ok_next = false;
     size_t off_next = 0;
@@ -405,7 +546,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_range(const void* base, i
 // are buffer loads with a per-block byte range, empty for a block that may not
 // be read, so they are unconditional.  The query fragments and the output
 // accumulators live in the accumulator file.
-template <int D>
+template <int D, bool FUSE>
 __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const Piece& pc,
                                float* lds) {
   constexpr int KS = D / 32;  // score products
@@ -447,6 +588,8 @@ __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const 
   const int* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk + j0 + wave;
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
+  NewToken<2, D> nt;
+  if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
   // this wave's table entries, 64 at a time (lane l: block tbase + l)
   int tbase = 0;
   int tbl = lane < nw ? bt[kWaves * lane] : 0;
@@ -483,6 +626,13 @@ __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const 
     load_v(rv);
     for (int i = 0; i < nw; ++i) {
       const int tok0 = (sp.first_blk + j0 + wave + kWaves * i) * kBlock;
+      if constexpr (FUSE) {
+        if (nt.own && i == nw - 1) {
+          nt.put_k(kb, lane);
+          nt.put_v(vb, lane);
+          nt.store(lane);
+        }
+      }
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int s = 0; s < KS; ++s) acc = mma_bf16_k32(kb[s], qf[s], acc);
@@ -559,7 +709,7 @@ constexpr int kRingBytesPerWave = 32768;
 // vector registers held by loads and no barrier in the loop.  A block is
 // copied verbatim (its K tile, then its V tile, 1 KiB per copy), so the
 // operands are read with the pool's own layouts.
-template <int D>
+template <int D, bool FUSE>
 __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const Piece& pc,
                                float* lds) {
   constexpr int KS = D / 32;                        // score products
@@ -601,6 +751,8 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
   char* ring = reinterpret_cast<char*>(lds) + wave * kRingBytesPerWave;
+  NewToken<2, D> nt;
+  if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
   // this wave's table entries, 64 at a time (lane l: block tbase + l)
   int tbase = 0;
   int tbl = lane < nw ? bt[kWaves * lane] : 0;
@@ -646,6 +798,9 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
     u32x4 kf[KS];
 #pragma unroll
     for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const u32x4*>(kt + (64 * s + lane) * 16);
+    const bool newtok = FUSE && nt.own && i == nw - 1;
+    if constexpr (FUSE)
+      if (newtok) nt.put_k(kf, lane);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < KS; ++s) acc = mma_bf16_k32(kf[s], qf[s], acc);
@@ -653,6 +808,12 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
 #pragma unroll
     for (int x = 0; x < XT; ++x)
       vf[x] = *reinterpret_cast<const u32x2*>(vt + (16 * x + c) * 2 * kBlock + 8 * j);
+    if constexpr (FUSE) {
+      if (newtok) {
+        nt.put_v(vf, lane);
+        nt.store(lane);
+      }
+    }
     mma_result_fence();
 
     float s2[4];
@@ -745,17 +906,18 @@ __device__ void finish_split(const DecodeArgs& a, int b, int g, SlotList slots, 
   __syncthreads();
 }
 
-template <bool BF16, int D, bool FIXED>
+template <bool BF16, int D, bool FIXED, bool FUSE>
 __global__ __launch_bounds__(kThreads, (BF16 && !kRingForm<D>) ? 2 : 1) void decode_kernel(DecodeArgs a) {
   extern __shared__ float lds[];
   auto run_one = [&](const LogitXform& xf, const Piece& pc) {
-    if constexpr (BF16)
+    if constexpr (BF16) {
       if constexpr (kRingForm<D>)
-        run_piece_ring<D>(a, xf, pc, lds);
+        run_piece_ring<D, FUSE>(a, xf, pc, lds);
       else
-        run_piece_bf16<D>(a, xf, pc, lds);
-    else
-      run_piece<BF16, D>(a, xf, pc, lds);
+        run_piece_bf16<D, FUSE>(a, xf, pc, lds);
+    } else {
+      run_piece<BF16, D, FUSE>(a, xf, pc, lds);
+    }
   };
   const LogitXform xf = make_xform(a.scale, a.softcap);
   const int Hkv = a.num_kv_heads, G = a.gqa_group;
@@ -864,6 +1026,14 @@ hipError_t allow_lds(K kernel, size_t lds) {
                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
 }
 
+template <typename K>
+hipError_t launch_k(K kernel, const DecodeArgs& a, size_t lds, hipStream_t stream) {
+  hipError_t e = allow_lds(kernel, lds);
+  if (e != hipSuccess) return e;
+  kernel<<<a.num_workers, kThreads, lds, stream>>>(a);
+  return hipGetLastError();
+}
+
 // Balanced-split grid: workgroups per CU, and a floor on the blocks a
 // workgroup gets (tiny batches use fewer workgroups).
 #ifndef PKV_DECODE_WGS_PER_CU
@@ -888,15 +1058,11 @@ hipError_t launch_d(DecodeArgs a, hipStream_t stream) {
   size_t lds = (size_t)kWaves * a.gqa_group * (D + 2) * sizeof(float);  // the waves' combine
   lds = std::max(lds, (size_t)(4 * kThreads + 2 * 16) * sizeof(float));  // a merge
   if (BF16 && kRingForm<D>) lds = std::max(lds, (size_t)kWaves * kRingBytesPerWave);
-  hipError_t e;
-  if (a.part_blocks > 0) {
-    if ((e = allow_lds(decode_kernel<BF16, D, true>, lds)) != hipSuccess) return e;
-    decode_kernel<BF16, D, true><<<a.num_workers, kThreads, lds, stream>>>(a);
-  } else {
-    if ((e = allow_lds(decode_kernel<BF16, D, false>, lds)) != hipSuccess) return e;
-    decode_kernel<BF16, D, false><<<a.num_workers, kThreads, lds, stream>>>(a);
-  }
-  return hipGetLastError();
+  if (a.part_blocks > 0)
+    return a.k_new ? launch_k(decode_kernel<BF16, D, true, true>, a, lds, stream)
+                   : launch_k(decode_kernel<BF16, D, true, false>, a, lds, stream);
+  return a.k_new ? launch_k(decode_kernel<BF16, D, false, true>, a, lds, stream)
+                 : launch_k(decode_kernel<BF16, D, false, false>, a, lds, stream);
 }
 
 template <bool BF16>

@@ -27,6 +27,10 @@ struct DecodeArgs {
   const void* q;
   const void* k_pool;
   const void* v_pool;
+  // fused append: the newest token's rows [num_seqs, num_kv_heads, head_dim];
+  // null for a plain decode (the pools are then only read)
+  const void* k_new;
+  const void* v_new;
   const int32_t* block_tables;
   const int32_t* context_lens;
   int32_t num_blocks;
@@ -89,5 +93,8 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, hipStre
 
 // Row tiles (of 16 GQA-packed query rows) per wave in the prefill kernel.
 int prefill_row_tiles(int head_dim, bool bf16);
+
+// Set the message pkv_last_error returns (on this thread); returns code.
+int record_error(int code, const char* fmt, ...);
 
 }  // namespace pkv

@@ -413,6 +413,19 @@ def chunked_prefill_shared_prefix(seed: int = 5, **kw) -> PrefillCase:
                              shared_prefix_blocks=64, scale=1.0 / 16.0, **kw)
 
 
+def random_bits(seed: int, shape, dtype: str) -> np.ndarray:
+    """N(0, 1) draws of ``shape`` as storage bits."""
+    return _normal_bits(np.random.default_rng(seed), shape, dtype)
+
+
+def new_token_rows(case: DecodeCase, seed: int):
+    """K and V rows ``[B, Hkv, D]`` (storage bits, N(0, 1)) of each sequence's
+    newest token, for a decode tick that appends them."""
+    rng = np.random.default_rng(seed)
+    shape = (case.num_seqs, case.num_kv_heads, case.head_dim)
+    return _normal_bits(rng, shape, case.dtype), _normal_bits(rng, shape, case.dtype)
+
+
 NAMED = {
     "tiny_decode_fp32": tiny_decode_fp32,
     "gemma_decode": gemma_decode,

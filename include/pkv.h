@@ -163,6 +163,76 @@ int paged_attn_decode_splitk(void* out, float* lse, const void* q, const void* k
                              size_t workspace_bytes, int32_t dtype, struct ihipStream_t* stream);
 
 /*
+ * paged_attn_decode_append -- one decode tick in one launch: the append of
+ * every sequence's newest token and the batched decode that attends to it.
+ * Each tick appends the token every active request just produced and runs
+ * one batched decode over all of them (page "Inference Server --
+ * Architecture Map", section "How a single request flows through the
+ * system"); the append writes into the block-paged pool (page "Inference
+ * Server", section "The engine").
+ *
+ * Arguments as paged_attn_decode (partition_size == 0) or
+ * paged_attn_decode_splitk (partition_size > 0), plus
+ *   k_new, v_new  [num_seqs, num_kv_heads, head_dim], the pool's dtype,
+ *                 16-byte aligned: the newest token's K and V rows
+ *   k_pool, v_pool  written as well as read
+ * Sequence b's newest token is position L_b - 1, L_b = min(context_lens[b],
+ * max_context_len, max_blocks_per_seq * 16) (so context_lens counts it); it
+ * goes to slot block_tables[b][(L_b - 1) / 16] * 16 + (L_b - 1) % 16 of every
+ * kv head, exactly as paged_kv_append with those slots would write it, and
+ * the outputs equal those of paged_kv_append followed by paged_attn_decode
+ * (or _splitk).  Sequences with L_b == 0, or whose entry for that block is
+ * outside [0, num_blocks), append nothing.  Within one call, no block that
+ * receives a token may be read by another sequence (a block shared by
+ * several sequences is copied before it is appended to).
+ * Errors as paged_attn_decode; PKV_EINVAL also for a missing or misaligned
+ * k_new / v_new.
+ */
+int paged_attn_decode_append(void* out, float* lse, const void* q, const void* k_new,
+                             const void* v_new, void* k_pool, void* v_pool, int32_t num_blocks,
+                             const int32_t* block_tables, int32_t max_blocks_per_seq,
+                             const int32_t* context_lens, int32_t max_context_len,
+                             int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                             int32_t head_dim, int32_t block_size, float scale, float softcap,
+                             int32_t window, int32_t partition_size, void* workspace,
+                             size_t workspace_bytes, int32_t dtype, struct ihipStream_t* stream);
+
+/*
+ * pkv_decode_graph -- a decode tick (paged_attn_decode_append) captured once
+ * into a HIP graph for one batch-size bucket and replayed every tick: the
+ * engine replays decode steps captured per batch-size bucket (page
+ * "Inference Server", section "The engine"), one batched decode per tick
+ * (page "Inference Server -- Architecture Map", section "How a single
+ * request flows through the system").
+ *
+ * pkv_decode_graph_create takes paged_attn_decode_append's arguments, minus
+ * the workspace and stream, for a bucket of num_seqs >= 1 rows.  Every
+ * pointer is bound into the graph: the caller keeps those buffers alive and
+ * in place until pkv_decode_graph_destroy, and before each launch writes the
+ * tick's q, k_new, v_new, block_tables and context_lens into them (rows the
+ * tick does not use: context_lens 0; they append nothing and output 0).
+ * max_context_len bounds every length of every tick.  The graph owns its
+ * decode workspace (allocated and zero-filled here, freed by destroy), so
+ * create allocates device memory and synchronises; launch does neither.
+ * Launches of one graph must not overlap (they share its workspace and
+ * buffers): launch on one stream, or order them.
+ *
+ * create: *graph = the new graph, or NULL on error (errors as
+ * paged_attn_decode_append, PKV_EHIP for a failed allocation or capture).
+ * launch: enqueues one replay on `stream`.  destroy: NULL is a no-op.
+ */
+typedef struct pkv_decode_graph pkv_decode_graph;
+int pkv_decode_graph_create(pkv_decode_graph** graph, void* out, float* lse, const void* q,
+                            const void* k_new, const void* v_new, void* k_pool, void* v_pool,
+                            int32_t num_blocks, const int32_t* block_tables,
+                            int32_t max_blocks_per_seq, const int32_t* context_lens,
+                            int32_t max_context_len, int32_t num_seqs, int32_t num_kv_heads,
+                            int32_t gqa_group, int32_t head_dim, int32_t block_size, float scale,
+                            float softcap, int32_t window, int32_t partition_size, int32_t dtype);
+int pkv_decode_graph_launch(pkv_decode_graph* graph, struct ihipStream_t* stream);
+void pkv_decode_graph_destroy(pkv_decode_graph* graph);
+
+/*
  * paged_attn_prefill -- causal attention of a chunk of new tokens over the
  * cached prefix plus the chunk (chunked / batched prefill, page "Inference
  * Server", section "The engine"; "Triton paged ... prefill kernels reading

@@ -20,14 +20,16 @@ pytestmark = pytest.mark.skipif(not os.path.exists(pkv.LIB_PATH),
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(?:int|size_t|const char\*)\s+(\w+)\s*\(", text)
+    names = re.findall(r"\b(?:int|void|size_t|const char\*)\s+(\w+)\s*\(", text)
     return sorted(set(names))
 
 
 def test_header_declares_the_entry_points():
     names = declared_functions()
     for n in ("paged_kv_append", "paged_attn_decode", "paged_attn_decode_splitk",
-              "paged_attn_prefill", "paged_attn_decode_workspace_size", "pkv_last_error"):
+              "paged_attn_decode_append", "paged_attn_prefill",
+              "paged_attn_decode_workspace_size", "pkv_decode_graph_create",
+              "pkv_decode_graph_launch", "pkv_decode_graph_destroy", "pkv_last_error"):
         assert n in names
     assert set(names) == set(pkv.SIGNATURES), "binding signatures out of sync with pkv.h"
 

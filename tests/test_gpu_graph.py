@@ -7,8 +7,9 @@ import pytest
 import torch
 
 import block_paged_kv_append_amd as pkv
+import oracle
 from block_paged_kv_append_amd import workloads as wl
-from tests.gpu_common import dev, i32
+from tests.gpu_common import as_f64, check_close, check_lse, dev, i32
 
 pytestmark = pytest.mark.gpu
 
@@ -67,3 +68,64 @@ def test_append_and_prefill_graph_replay():
         pkv.paged_attn_prefill(out, q, cu, p.max_q_len, kp, vp, bt, cl, p.max_context_len, p.scale)
 
     _replays_match(fn, out)
+
+
+@pytest.mark.parametrize("D,P", [(128, 0), (256, 0), (256, 64)])
+def test_decode_tick_graph_bucket(D, P):
+    """One bucket of 8 rows captured once (pkv_decode_graph) and replayed for
+    three ticks of a decode loop with 8, 5 and 3 active sequences: each tick
+    writes new q rows, new K/V rows and lengths one longer into the bound
+    buffers; inactive rows have length 0.  Every replay against the oracle's
+    tick, the pools carried over from tick to tick."""
+    final = [300, 17, 900, 3, 64, 700, 31, 2000]
+    Bb, Hq, Hkv, T = 8, 8, 2, 3
+    case = wl.make_decode_case(510 + D + P, final, Hq, Hkv, D, "bf16", softcap=20.0)
+    assert pkv.decode_bucket(5) == Bb and pkv.decode_bucket(8) == Bb
+    q = torch.empty((Bb, Hq, D), dtype=torch.bfloat16, device="cuda")
+    kn = torch.empty((Bb, Hkv, D), dtype=torch.bfloat16, device="cuda")
+    vn = torch.empty_like(kn)
+    kp, vp = dev(case.k_pool, "bf16"), dev(case.v_pool, "bf16")
+    bt = i32(case.block_tables)
+    cl = torch.zeros(Bb, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((Bb, Hq), dtype=torch.float32, device="cuda")
+    graph = pkv.DecodeGraph(out, q, kn, vn, kp, vp, bt, cl, max(final), case.scale, case.softcap,
+                            partition_size=P, lse=lse)
+    kr, vr = case.k_pool, case.v_pool
+    for t, active in enumerate([8, 5, 3]):
+        print(f"\n[case] decode tick graph D={D} P={P} tick {t} active {active}", flush=True)
+        lens = np.array([final[b] - T + 1 + t if b < active else 0 for b in range(Bb)],
+                        dtype=np.int32)
+        q_t = wl.random_bits(520 + t, (Bb, Hq, D), "bf16")
+        kn_t = wl.random_bits(530 + t, (Bb, Hkv, D), "bf16")
+        vn_t = wl.random_bits(540 + t, (Bb, Hkv, D), "bf16")
+        q.copy_(dev(q_t, "bf16"))
+        kn.copy_(dev(kn_t, "bf16"))
+        vn.copy_(dev(vn_t, "bf16"))
+        cl.copy_(i32(lens))
+        out.fill_(float("nan"))
+        graph.launch()
+        torch.cuda.synchronize()
+        ref, ref_lse, kr, vr = oracle.decode_append(q_t, kn_t, vn_t, kr, vr, case.block_tables,
+                                                    lens, case.scale, case.softcap, 0, "bf16")
+        check_close(as_f64(out), ref, "bf16", f"tick {t}")
+        check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, f"tick {t}")
+        assert (as_f64(out)[active:] == 0).all()
+        _ = (torch.randn(1000, device="cuda") * 2).sum().item()  # eager work in between
+    assert np.array_equal(pkv.to_bits(kp), kr) and np.array_equal(pkv.to_bits(vp), vr)
+    graph.close()
+
+
+def test_decode_graph_rejects_bad_arguments():
+    case = wl.make_decode_case(550, [20, 40], 4, 1, 64, "bf16")
+    q = dev(case.q, "bf16")
+    kp, vp = dev(case.k_pool, "bf16"), dev(case.v_pool, "bf16")
+    kn = torch.zeros((2, 1, 64), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty_like(q)
+    bt, cl = i32(case.block_tables), i32(case.context_lens)
+    with pytest.raises(pkv.PkvError):
+        pkv.DecodeGraph(out, q, kn, kn, kp, vp, bt, cl, case.max_context_len, case.scale,
+                        partition_size=24)
+    lib = pkv.load_library()
+    assert lib.pkv_decode_graph_launch(None, None) == -1
+    lib.pkv_decode_graph_destroy(None)

@@ -141,6 +141,30 @@ def test_decode_poisoned_table_padding_is_never_read():
     check_close(out, oracle_decode(case)[0], "bf16", "boundary")
 
 
+def test_decode_more_workgroups_than_blocks():
+    """A max_context_len far above the actual lengths sizes the grid for more
+    workgroups than there are blocks (each then gets one block or none); the
+    segments split one block per workgroup must still be merged, and leave
+    the workspace's counters at zero for the next call."""
+    case = wl.make_decode_case(351, [100, 40, 300, 17], 8, 2, 128, "bf16", softcap=10.0,
+                               max_blocks_per_seq=256)
+    ref, ref_lse = oracle_decode(case)
+    q, kp, vp = dev(case.q, "bf16"), dev(case.k_pool, "bf16"), dev(case.v_pool, "bf16")
+    bt, cl = i32(case.block_tables), i32(case.context_lens)
+    ws = torch.zeros(pkv.paged_attn_decode_workspace_size(4, 2, 4, 128, 4096, 0),
+                     dtype=torch.uint8, device="cuda")
+    for rep in range(3):
+        banner("decode N > W", rep)
+        out = torch.full_like(q, float("nan"))
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+        pkv.paged_attn_decode(out, q, kp, vp, bt, cl, 4096, case.scale, case.softcap, 0,
+                              lse=lse, workspace=ws)
+        torch.cuda.synchronize()
+        check_close(out.float().cpu().numpy().astype(np.float64), ref, "bf16", f"N > W {rep}")
+        check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, f"N > W {rep}")
+    assert int(ws[:4 * 8].view(torch.int32).abs().sum()) == 0  # counters back at zero
+
+
 # ---------------------------------------------------------------------------
 # the named workloads at full size
 # ---------------------------------------------------------------------------
