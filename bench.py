@@ -37,8 +37,8 @@ BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 METRIC = "paged-decode KV GB/s (% HBM peak) + tok/s; paged-prefill TFLOP/s at 1 GPU"
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
-    "decode": ["decode.hip", "attn_tile.hpp", "common.hpp", "api.cpp"],
-    "prefill": ["prefill.hip", "attn_tile.hpp", "common.hpp", "api.cpp"],
+    "decode": ["decode.hip", "attn_tile.hpp", "common.hpp", "launch.hpp", "api.cpp"],
+    "prefill": ["prefill.hip", "attn_tile.hpp", "common.hpp", "launch.hpp", "api.cpp"],
 }
 
 
@@ -51,6 +51,8 @@ def parse_args():
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--quick", action="store_true", help="headline step only")
+    p.add_argument("--prefill-only", action="store_true",
+                   help="only the chunk append and prefill timing (for counter runs)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain device copy of known size (HBM counter calibration)")
     return p.parse_args()
@@ -223,17 +225,23 @@ def time_steps(bench, steps, warmup, step, torch):
     return (time.perf_counter() - t0) * steps / (reps * bench.R)
 
 
+OP_CALLS = 24  # calls per timed graph replay: the replay's own start-up is spread over them
+
+
 def time_decode_op(bench, iters, torch, op=None):
     """Average duration of one decode operation (``op(r)``, by default the
-    plain decode): a graph of R calls (one per replica) replayed ``iters``
-    times, each replay bracketed by HIP events on the stream, divided by R."""
+    plain decode): a graph of about OP_CALLS calls cycling over the R pool
+    replicas, replayed ``iters`` times, each replay bracketed by HIP events on
+    the stream, divided by the calls per replay."""
     import numpy as np
 
     op = op or bench.decode
+    rounds = max(1, OP_CALLS // bench.R)
 
     def all_decodes():
-        for r in range(bench.R):
-            op(r)
+        for _ in range(rounds):
+            for r in range(bench.R):
+                op(r)
 
     all_decodes()
     torch.cuda.synchronize()
@@ -246,10 +254,11 @@ def time_decode_op(bench, iters, torch, op=None):
         g.replay()
         ev[i][1].record()
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev])) / bench.R
+    return float(np.mean([a.elapsed_time(b) for a, b in ev])) / (rounds * bench.R)
 
 
 APPEND_REPEAT = 16  # appends per graph replay: one alone is shorter than a launch
+PREFILL_REPEAT = 8  # prefills per graph replay (each recomputes the same output)
 
 
 def time_prefill(case, iters, warmup, torch, pkv):
@@ -273,8 +282,9 @@ def time_prefill(case, iters, warmup, torch, pkv):
             pkv.paged_kv_append(k_new, v_new, slots, kp, vp)
 
     def prefill():
-        pkv.paged_attn_prefill(out, q, cu, case.max_q_len, kp, vp, bt, cl, case.max_context_len,
-                               case.scale, case.softcap, case.window)
+        for _ in range(PREFILL_REPEAT):
+            pkv.paged_attn_prefill(out, q, cu, case.max_q_len, kp, vp, bt, cl,
+                                   case.max_context_len, case.scale, case.softcap, case.window)
 
     append()
     prefill()
@@ -293,7 +303,28 @@ def time_prefill(case, iters, warmup, torch, pkv):
             ev[i][1].record()
         torch.cuda.synchronize()
         res.append(float(np.mean([a.elapsed_time(b) for a, b in ev])))
-    return res[0] / APPEND_REPEAT, res[1]
+    return res[0] / APPEND_REPEAT, res[1] / PREFILL_REPEAT
+
+
+def copy_rate(torch) -> float:
+    """GB/s (bytes read + written) of a plain 1 GiB device copy right now: the
+    bandwidth this GPU delivers to a trivial kernel, as context for the rates
+    above (it varies from one machine to another)."""
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 20
+    del a, b
+    torch.cuda.empty_cache()
+    return 2 * n / (ms * 1e-3) / 1e9
 
 
 def calibrate_copy(torch):
@@ -357,6 +388,11 @@ def main():
     pkv.load_library()  # raises if libpkv.so is missing: there is no fallback
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.prefill_only:
+        pc = wl.chunked_prefill_shared_prefix()
+        app_ms, pre_ms = time_prefill(pc, 20, 3, torch, pkv)
+        print(json.dumps({"prefill_ms": round(pre_ms, 5), "append_ms": round(app_ms, 5)}))
         return
 
     t_setup = time.perf_counter()
@@ -438,6 +474,8 @@ def main():
             torch.cuda.empty_cache()
         line["other_workloads"] = extra
 
+    if not args.quick:
+        line["box_copy_gbs"] = round(copy_rate(torch), 1)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
