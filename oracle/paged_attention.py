@@ -326,3 +326,33 @@ def decode_append(q, k_new, v_new, k_pool, v_pool, block_tables, context_lens, s
     out, lse = decode(q, kp, vp, block_tables, context_lens, scale, softcap, window, dtype)
     return out, lse, kp, vp
 
+
+# ---------------------------------------------------------------------------
+# [engine] copy-on-write of refcounted shared blocks
+# ---------------------------------------------------------------------------
+def copy_blocks(src_ids, dst_ids, k_pool, v_pool):
+    """Copies of the pools in which block ``dst_ids[i]`` holds what block
+    ``src_ids[i]`` held before the call, in both pools, for every kv head and
+    all 16 slots ([engine]: blocks are refcounted and shared between
+    sequences; one that writes into a shared block first gets its own copy).
+    Pairs with ``src == dst`` or an id outside the pool are skipped.
+
+    Raises ``ValueError`` if a destination repeats or is also a source (the
+    result would depend on the order of the copies)."""
+    NB = k_pool.shape[0]
+    src = [int(x) for x in np.asarray(src_ids).tolist()]
+    dst = [int(x) for x in np.asarray(dst_ids).tolist()]
+    if len(src) != len(dst):
+        raise ValueError("src_ids and dst_ids differ in length")
+    live = [(s_, d_) for s_, d_ in zip(src, dst) if 0 <= s_ < NB and 0 <= d_ < NB and s_ != d_]
+    dsts = [d_ for _, d_ in live]
+    if len(set(dsts)) != len(dsts):
+        raise ValueError("a destination block repeats")
+    if set(dsts) & {s_ for s_, _ in live}:
+        raise ValueError("a destination block is also a source")
+    kp, vp = k_pool.copy(), v_pool.copy()
+    for s_, d_ in live:
+        kp[d_] = k_pool[s_]
+        vp[d_] = v_pool[s_]
+    return kp, vp
+

@@ -419,6 +419,46 @@ def test_p9_shared_prefix_equals_private_copies():
 
 
 # ---------------------------------------------------------------------------
+# P14 copy-on-write block copy
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_p14_copied_block_gathers_the_same_rows(dtype):
+    """A sequence whose table entry j is swapped for a copy of block table[j]
+    gathers exactly the same K/V rows; the copy is checked element by element
+    against the pool layout, and every other block is untouched."""
+    case = wl.make_decode_case(1400, [40, 70], 4, 2, 16, dtype, pool_factor=2.0)
+    b, j = 1, 2
+    src = int(case.block_tables[b, j])
+    free = sorted(set(range(case.num_blocks)) - set(case.block_tables[:, :5].ravel().tolist()))
+    dst = free[0]
+    kp, vp = oracle.copy_blocks([src, 3, 5], [dst, 3, case.num_blocks], case.k_pool, case.v_pool)
+    X = 16 // wl.elem_bytes(dtype)
+    for g in range(2):
+        for d in range(16):
+            for o in range(16):
+                assert kp[dst, g, d // X, o, d % X] == case.k_pool[src, g, d // X, o, d % X]
+                assert vp[dst, g, d, o] == case.v_pool[src, g, d, o]
+    others = [i for i in range(case.num_blocks) if i != dst]
+    assert np.array_equal(kp[others].view(np.uint8), case.k_pool[others].view(np.uint8))
+    assert np.array_equal(vp[others].view(np.uint8), case.v_pool[others].view(np.uint8))
+    row = case.block_tables[b].copy()
+    row[j] = dst
+    L = int(case.context_lens[b])
+    K0, V0 = oracle.gather_sequence(case.k_pool, case.v_pool, case.block_tables[b], L, 1, dtype)
+    K1, V1 = oracle.gather_sequence(kp, vp, row, L, 1, dtype)
+    np.testing.assert_array_equal(K0, K1)
+    np.testing.assert_array_equal(V0, V1)
+
+
+def test_p14_copy_blocks_rejects_ambiguous_pairs():
+    case = wl.make_decode_case(1401, [40], 2, 1, 16, "bf16", pool_factor=3.0)
+    with pytest.raises(ValueError):
+        oracle.copy_blocks([0, 1], [4, 4], case.k_pool, case.v_pool)
+    with pytest.raises(ValueError):
+        oracle.copy_blocks([0, 4], [4, 5], case.k_pool, case.v_pool)
+
+
+# ---------------------------------------------------------------------------
 # P10 append
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
