@@ -26,6 +26,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -36,9 +37,10 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
 METRIC = "paged-decode KV GB/s (% HBM peak) + tok/s; paged-prefill TFLOP/s at 1 GPU"
 PROFILES = os.path.join(ROOT, "profiles")
+# what a kernel's HBM counters depend on: its sources and its argument struct
 KERNEL_SOURCES = {
-    "decode": ["decode.hip", "attn_tile.hpp", "common.hpp", "launch.hpp", "api.cpp"],
-    "prefill": ["prefill.hip", "attn_tile.hpp", "common.hpp", "launch.hpp", "api.cpp"],
+    "decode": (["decode.hip", "attn_tile.hpp", "common.hpp"], "DecodeArgs"),
+    "prefill": (["prefill.hip", "attn_tile.hpp", "common.hpp"], "PrefillArgs"),
 }
 
 
@@ -59,10 +61,15 @@ def parse_args():
 
 
 def source_sha(kind: str) -> str:
+    files, args_struct = KERNEL_SOURCES[kind]
+    csrc = os.path.join(ROOT, "block_paged_kv_append_amd", "csrc")
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "block_paged_kv_append_amd", "csrc", f), "rb") as fh:
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
+    with open(os.path.join(csrc, "launch.hpp")) as fh:
+        m = re.search(r"struct %s \{.*?\n\};" % args_struct, fh.read(), re.S)
+    h.update(m.group(0).encode() if m else b"")
     return h.hexdigest()[:16]
 
 
@@ -306,6 +313,45 @@ def time_prefill(case, iters, warmup, torch, pkv):
     return res[0] / APPEND_REPEAT, res[1] / PREFILL_REPEAT
 
 
+COPY_PAIRS = 512  # copy-on-write pairs per call in the block-copy measurement
+
+
+def time_copy_blocks(bench, iters, torch):
+    """Average duration of one paged_kv_copy_blocks call copying COPY_PAIRS
+    whole blocks (disjoint random sources and destinations) of the decode
+    bench's pools: a graph of one call per pool replica, replayed ``iters``
+    times, each replay bracketed by HIP events.  Run after the decode
+    timings (it overwrites blocks)."""
+    import numpy as np
+
+    case, pkv = bench.case, bench.pkv
+    NB = case.num_blocks
+    perm = np.random.default_rng(77).permutation(NB)
+    n = min(COPY_PAIRS, NB // 2)
+    pairs = [(torch.from_numpy((perm[:n] + r * NB).astype(np.int32)).cuda(),
+              torch.from_numpy((perm[n:2 * n] + r * NB).astype(np.int32)).cuda())
+             for r in range(bench.R)]
+
+    def copies():
+        for src, dst in pairs:
+            pkv.paged_kv_copy_blocks(src, dst, bench.kp, bench.vp)
+
+    copies()
+    torch.cuda.synchronize()
+    g = capture(torch, copies)
+    warm(g, torch, 0.2)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(iters)]
+    for i in range(iters):
+        ev[i][0].record()
+        g.replay()
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev])) / bench.R
+    per_pair = 2 * case.num_kv_heads * case.head_dim * 16 * (2 if case.dtype == "bf16" else 4)
+    return ms, n, 2 * n * per_pair  # bytes read + written
+
+
 def copy_rate(torch) -> float:
     """GB/s (bytes read + written) of a plain 1 GiB device copy right now: the
     bandwidth this GPU delivers to a trivial kernel, as context for the rates
@@ -461,6 +507,10 @@ def main():
                        "bytes": ab},
         }
         del pc
+        cb_ms, cb_pairs, cb_bytes = time_copy_blocks(bench, 20, torch)
+        line["copy_blocks"] = {"pairs": cb_pairs, "ms": round(cb_ms, 5),
+                               "gbs": round(cb_bytes / (cb_ms * 1e-3) / 1e9, 1), "bytes": cb_bytes,
+                               "pool": "gemma_decode (2 kv heads, D256, bf16: 32 KiB per pair)"}
         for maker in (wl.sliding_window_decode, wl.long_context_splitk):
             c = maker()
             b = DecodeBench(c, 0, torch, pkv)

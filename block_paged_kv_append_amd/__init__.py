@@ -26,12 +26,21 @@ PKV_BF16 = 1
 BLOCK_SIZE = 16
 
 _STATUS = {0: "PKV_OK", -1: "PKV_EINVAL", -2: "PKV_EUNSUPPORTED", -3: "PKV_EWORKSPACE",
-           -4: "PKV_EHIP"}
+           -4: "PKV_EHIP", -5: "PKV_ENOMEM"}
 
 # (name, restype, argtypes) of every entry point in include/pkv.h
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "paged_kv_append": (ctypes.c_int, [_P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _P]),
+    "paged_kv_copy_blocks": (ctypes.c_int, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _I, _P]),
+    "pkv_allocator_create": (ctypes.c_int, [ctypes.POINTER(_P), _I]),
+    "pkv_allocator_destroy": (None, [_P]),
+    "pkv_allocator_alloc": (ctypes.c_int, [_P, _I, _P]),
+    "pkv_allocator_share": (ctypes.c_int, [_P, _P, _I]),
+    "pkv_allocator_release": (ctypes.c_int, [_P, _P, _I]),
+    "pkv_allocator_prepare_write": (ctypes.c_int, [_P, _P, _I, _I, _P, _P, _P]),
+    "pkv_allocator_num_free": (_I, [_P]),
+    "pkv_allocator_refcount": (_I, [_P, _I]),
     "paged_attn_decode_workspace_size": (_Z, [_I, _I, _I, _I, _I, _I]),
     "paged_attn_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I, _I, _I,
                                          _I, _F, _F, _I, _P, _Z, _I, _P]),
@@ -159,6 +168,86 @@ def paged_kv_append(k_new, v_new, slot_mapping, k_pool, v_pool, stream=None) -> 
                              _ptr(k_pool), _ptr(v_pool), nb, hkv, d, BLOCK_SIZE,
                              _dtype_code(k_pool), _stream(stream))
     _check("paged_kv_append", rc)
+
+
+def paged_kv_copy_blocks(src_ids, dst_ids, k_pool, v_pool, stream=None) -> None:
+    """Copy whole blocks ``src_ids[i] -> dst_ids[i]`` (int32 device tensors) in
+    both pools (copy-on-write of shared blocks)."""
+    nb, hkv, d = _pool_dims(k_pool, v_pool)
+    n = src_ids.numel()
+    if dst_ids.numel() != n:
+        raise ValueError("src_ids and dst_ids must have the same length")
+    lib = load_library()
+    rc = lib.paged_kv_copy_blocks(_ptr(k_pool), _ptr(v_pool), nb, hkv, d, BLOCK_SIZE,
+                                  _i32(src_ids, "src_ids"), _i32(dst_ids, "dst_ids"), n,
+                                  _dtype_code(k_pool), _stream(stream))
+    _check("paged_kv_copy_blocks", rc)
+
+
+class BlockAllocator:
+    """Host-side refcounted block ids with copy-on-write (``pkv_block_allocator``
+    in include/pkv.h).  Ids and table rows are numpy int32 arrays."""
+
+    def __init__(self, num_blocks: int):
+        self._lib = load_library()
+        h = ctypes.c_void_p()
+        _check("pkv_allocator_create", self._lib.pkv_allocator_create(ctypes.byref(h),
+                                                                      int(num_blocks)))
+        self._h = h
+
+    @staticmethod
+    def _arr(ids):
+        import numpy as np
+
+        a = np.ascontiguousarray(ids, dtype=np.int32)
+        return a, a.ctypes.data_as(ctypes.c_void_p)
+
+    def alloc(self, n: int):
+        import numpy as np
+
+        out = np.empty(int(n), dtype=np.int32)
+        _check("pkv_allocator_alloc", self._lib.pkv_allocator_alloc(
+            self._h, int(n), out.ctypes.data_as(ctypes.c_void_p)))
+        return out
+
+    def share(self, ids) -> None:
+        a, p = self._arr(ids)
+        _check("pkv_allocator_share", self._lib.pkv_allocator_share(self._h, p, a.size))
+
+    def release(self, ids) -> None:
+        a, p = self._arr(ids)
+        _check("pkv_allocator_release", self._lib.pkv_allocator_release(self._h, p, a.size))
+
+    def prepare_write(self, table_row, first: int, last: int):
+        """Copy-on-write for logical blocks ``[first, last]`` of ``table_row``
+        (an int32 numpy array, updated in place); returns the (src, dst) pairs
+        to copy."""
+        import numpy as np
+
+        if table_row.dtype != np.int32 or not table_row.flags.c_contiguous:
+            raise TypeError("table_row must be a contiguous int32 numpy array")
+        n = max(int(last) - int(first) + 1, 0)
+        src, dst = np.empty(n, dtype=np.int32), np.empty(n, dtype=np.int32)
+        cnt = ctypes.c_int32(0)
+        _check("pkv_allocator_prepare_write", self._lib.pkv_allocator_prepare_write(
+            self._h, table_row.ctypes.data_as(ctypes.c_void_p), int(first), int(last),
+            src.ctypes.data_as(ctypes.c_void_p), dst.ctypes.data_as(ctypes.c_void_p),
+            ctypes.byref(cnt)))
+        return src[:cnt.value].copy(), dst[:cnt.value].copy()
+
+    def num_free(self) -> int:
+        return int(self._lib.pkv_allocator_num_free(self._h))
+
+    def refcount(self, block: int) -> int:
+        return int(self._lib.pkv_allocator_refcount(self._h, int(block)))
+
+    def close(self) -> None:
+        if getattr(self, "_h", None) is not None:
+            self._lib.pkv_allocator_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
 
 
 def paged_attn_decode_workspace_size(num_seqs, num_kv_heads, gqa_group, head_dim,

@@ -13,7 +13,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
-SOURCES = ["api.cpp", "graph.cpp", "append.hip", "decode.hip", "prefill.hip"]
+SOURCES = ["api.cpp", "graph.cpp", "allocator.cpp", "append.hip", "blocks.hip", "decode.hip",
+           "prefill.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

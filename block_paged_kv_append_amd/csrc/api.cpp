@@ -242,6 +242,35 @@ int paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot_ma
   return from_hip(pkv::launch_append(a, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+int paged_kv_copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, const int32_t* src_ids,
+                         const int32_t* dst_ids, int32_t num_pairs, int32_t dtype,
+                         struct ihipStream_t* stream) {
+  const char* fn = "paged_kv_copy_blocks";
+  const int es = elem_bytes(dtype);
+  if (es == 0) return fail(PKV_EUNSUPPORTED, "%s: dtype %d", fn, dtype);
+  if (block_size != PKV_BLOCK_SIZE)
+    return fail(PKV_EUNSUPPORTED, "%s: block_size %d (only 16)", fn, block_size);
+  if (!head_dim_ok(head_dim)) return fail(PKV_EUNSUPPORTED, "%s: head_dim %d", fn, head_dim);
+  if (num_pairs < 0 || num_blocks < 0 || num_kv_heads < 1)
+    return fail(PKV_EINVAL, "%s: num_pairs %d, num_blocks %d, num_kv_heads %d", fn, num_pairs,
+                num_blocks, num_kv_heads);
+  if (num_pairs == 0) return PKV_OK;
+  if (!k_pool || !v_pool || !src_ids || !dst_ids)
+    return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (!aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(src_ids, 4) || !aligned(dst_ids, 4))
+    return fail(PKV_EINVAL, "%s: misaligned pointer", fn);
+  pkv::CopyBlocksArgs a{};
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.src_ids = src_ids;
+  a.dst_ids = dst_ids;
+  a.num_pairs = num_pairs;
+  a.num_blocks = num_blocks;
+  a.block_bytes = (size_t)num_kv_heads * head_dim * PKV_BLOCK_SIZE * es;
+  return from_hip(pkv::launch_copy_blocks(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
                                         int32_t gqa_group, int32_t head_dim,
                                         int32_t max_context_len, int32_t partition_size) {

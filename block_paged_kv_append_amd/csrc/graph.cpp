@@ -56,7 +56,7 @@ int pkv_decode_graph_create(pkv_decode_graph** graph, void* out, float* lse, con
                       "head_dim %d, max_context_len %d, partition_size %d)", fn, num_seqs,
                       num_kv_heads, gqa_group, head_dim, max_context_len, partition_size);
   pkv_decode_graph* g = new (std::nothrow) pkv_decode_graph();
-  if (g == nullptr) return record_error(PKV_EHIP, "%s: out of host memory", fn);
+  if (g == nullptr) return record_error(PKV_ENOMEM, "%s: out of host memory", fn);
 
   hipStream_t s = nullptr;
   hipError_t e = hipMalloc(&g->workspace, ws_bytes);

@@ -21,6 +21,16 @@ struct AppendArgs {
   int32_t elem_bytes;  // 2 (bf16) or 4 (fp32)
 };
 
+struct CopyBlocksArgs {
+  void* k_pool;
+  void* v_pool;
+  const int32_t* src_ids;
+  const int32_t* dst_ids;
+  int32_t num_pairs;
+  int32_t num_blocks;
+  size_t block_bytes;  // one block of one pool: num_kv_heads * head_dim * 16 * element bytes
+};
+
 struct DecodeArgs {
   void* out;
   float* lse;  // may be null
@@ -88,6 +98,7 @@ size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t gq
                               int32_t head_dim, int32_t max_context_len, int32_t partition_size);
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, hipStream_t stream);
 

@@ -72,7 +72,9 @@ enum pkv_status {
                             gqa_group outside what the entry point supports,
                             partition_size not a positive multiple of 16        */
   PKV_EWORKSPACE = -3,   /* workspace null or smaller than the size query says  */
-  PKV_EHIP = -4          /* the HIP runtime reported an error at launch         */
+  PKV_EHIP = -4,         /* the HIP runtime reported an error at launch         */
+  PKV_ENOMEM = -5        /* the block allocator has too few free blocks, or the
+                            host is out of memory                               */
 };
 
 #define PKV_BLOCK_SIZE 16
@@ -95,6 +97,62 @@ int paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot_ma
                     int32_t num_tokens, void* k_pool, void* v_pool, int32_t num_blocks,
                     int32_t num_kv_heads, int32_t head_dim, int32_t block_size, int32_t dtype,
                     struct ihipStream_t* stream);
+
+/*
+ * paged_kv_copy_blocks -- copy-on-write block copies inside the pools.  The
+ * cache is block-paged with refcounted blocks (page "Inference Server",
+ * section "The engine"): sequences that share a prefix hold the same
+ * physical blocks, and a sequence about to write into a shared block first
+ * gets a private copy of it.  This copies, for each pair i, the whole block
+ * src_ids[i] to block dst_ids[i] in both pools (every kv head, all 16 slots).
+ *
+ *   k_pool, v_pool  the pools (paged_kv_append's layout), updated in place
+ *   src_ids, dst_ids  int32 [num_pairs] device arrays
+ * A pair with an id outside [0, num_blocks), or with src == dst, is skipped.
+ * The destinations must be distinct and none may be a source of another
+ * pair (otherwise the result depends on the order of the copies).  The copy
+ * is bit-exact.  num_pairs == 0 is a no-op.
+ */
+int paged_kv_copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks, int32_t num_kv_heads,
+                         int32_t head_dim, int32_t block_size, const int32_t* src_ids,
+                         const int32_t* dst_ids, int32_t num_pairs, int32_t dtype,
+                         struct ihipStream_t* stream);
+
+/*
+ * pkv_block_allocator -- the host side of refcounted blocks (page "Inference
+ * Server", section "The engine"): hands out block ids, counts the block
+ * tables holding each block, and prepares copy-on-write before a sequence
+ * writes into blocks it shares.  Host memory only, no HIP calls; every
+ * function locks the allocator, so calls from several threads are safe.
+ *
+ *   create: an allocator of num_blocks ids, all free (handed out 0, 1, ...).
+ *   alloc: n fresh ids (refcount 1) into ids[0..n); all or nothing
+ *     (PKV_ENOMEM if fewer than n are free).
+ *   share: one more holder for each listed id (a table that now also holds
+ *     it, e.g. a forked prefix); every id must be allocated.
+ *   release: one holder fewer for each listed id (repeats count); a block
+ *     whose count reaches 0 is free again.  All or nothing.
+ *   prepare_write: a sequence is about to write into logical blocks
+ *     [first, last] of its table row (host memory).  Every such block held
+ *     by more than one table is replaced in table_row by a fresh private
+ *     block; the pair (old, new) is written to src_ids / dst_ids (room for
+ *     last - first + 1 pairs) and counted in *num_copies; the old block loses
+ *     this holder.  The caller then copies the pairs with
+ *     paged_kv_copy_blocks before writing.  All or nothing (PKV_ENOMEM if
+ *     too few blocks are free).
+ *   num_free, refcount: -1 for a null allocator or an out-of-range id.
+ */
+typedef struct pkv_block_allocator pkv_block_allocator;
+int pkv_allocator_create(pkv_block_allocator** allocator, int32_t num_blocks);
+void pkv_allocator_destroy(pkv_block_allocator* allocator);
+int pkv_allocator_alloc(pkv_block_allocator* allocator, int32_t n, int32_t* ids);
+int pkv_allocator_share(pkv_block_allocator* allocator, const int32_t* ids, int32_t n);
+int pkv_allocator_release(pkv_block_allocator* allocator, const int32_t* ids, int32_t n);
+int pkv_allocator_prepare_write(pkv_block_allocator* allocator, int32_t* table_row, int32_t first,
+                                int32_t last, int32_t* src_ids, int32_t* dst_ids,
+                                int32_t* num_copies);
+int32_t pkv_allocator_num_free(pkv_block_allocator* allocator);
+int32_t pkv_allocator_refcount(pkv_block_allocator* allocator, int32_t block);
 
 /*
  * paged_attn_decode_workspace_size -- bytes of device workspace that

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(pkv.LIB_PATH),
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    names = re.findall(r"\b(?:int|void|size_t|const char\*)\s+(\w+)\s*\(", text)
+    names = re.findall(r"\b(?:int|int32_t|void|size_t|const char\*)\s+(\w+)\s*\(", text)
     return sorted(set(names))
 
 
