@@ -8,6 +8,7 @@ from .paged_attention import (  # noqa: F401
     BLOCK,
     append,
     attend,
+    column_mass,
     copy_blocks,
     decode,
     decode_append,

@@ -39,6 +39,12 @@ Readings taken where the pages are silent (each is listed in the design doc too):
   ``cap <= 0`` meaning off;
 * a sliding window of ``W`` [engine] keeps key ``t`` iff ``q_pos - t < W``
   (the last W tokens, the query's own included); ``W <= 0`` means off;
+* the AttentionSink policy [inside] keeps the first ``sink`` tokens beside
+  the window (StreamingLLM's sink tokens); without a window it changes
+  nothing;
+* the H2O policy [inside] ranks tokens by the attention they receive: a
+  decode step contributes, per token and kv head, the softmax weights of the
+  query heads of that group, summed;
 * prefill queries are the last ``n_b`` of the ``L_b`` tokens:
   ``q_pos = L_b - n_b + j`` and keys must satisfy ``t <= q_pos``;
 * split-K [engine] partitions are anchored at token 0 and merged by
@@ -94,17 +100,20 @@ def gather_sequence(k_pool, v_pool, table_row, n_tokens: int, kv_head: int, dtyp
 # ---------------------------------------------------------------------------
 # masks and scores
 # ---------------------------------------------------------------------------
-def visible(q_pos: int, n_keys: int, window: int = 0, causal: bool = True) -> np.ndarray:
+def visible(q_pos: int, n_keys: int, window: int = 0, causal: bool = True,
+            sink: int = 0) -> np.ndarray:
     """Boolean mask over keys ``0 .. n_keys-1`` seen by a query at ``q_pos``:
     key ``t`` is kept iff it exists (``t < n_keys``), is not in the future
     (``t <= q_pos``, causal prefill), and, for a window-aware sliding layer
-    [engine], lies among the last ``window`` positions (``q_pos - t < window``)."""
+    [engine], lies among the last ``window`` positions (``q_pos - t < window``)
+    or, with the AttentionSink policy [inside], among the first ``sink``
+    tokens (``t < sink``)."""
     t = np.arange(n_keys)
     keep = np.ones(n_keys, dtype=bool)
     if causal:
         keep &= t <= q_pos
     if window > 0:
-        keep &= (q_pos - t) < window
+        keep &= ((q_pos - t) < window) | (t < sink)
     return keep
 
 
@@ -117,7 +126,7 @@ def scores(q_rows: np.ndarray, K: np.ndarray, scale: float, softcap: float = 0.0
     return s
 
 
-def attend(q_rows, K, V, q_pos, scale, softcap=0.0, window=0, causal=True):
+def attend(q_rows, K, V, q_pos, scale, softcap=0.0, window=0, causal=True, sink=0):
     """softmax(scores) @ V over the visible keys, one query row at a time.
 
     Returns ``out [R, D]`` and the natural-log ``lse [R]``; a row that sees no
@@ -130,7 +139,7 @@ def attend(q_rows, K, V, q_pos, scale, softcap=0.0, window=0, causal=True):
     if n == 0:
         return out, lse
     s = scores(q_rows, K, scale, softcap)
-    keep = np.stack([visible(int(q_pos[r]), n, window, causal) for r in range(R)])
+    keep = np.stack([visible(int(q_pos[r]), n, window, causal, sink) for r in range(R)])
     any_key = keep.any(axis=1)
     s = np.where(keep, s, -np.inf)
     m = np.where(any_key, s.max(axis=1), 0.0)
@@ -146,7 +155,7 @@ def attend(q_rows, K, V, q_pos, scale, softcap=0.0, window=0, causal=True):
 # [engine]/[flow] batched one-token decode
 # ---------------------------------------------------------------------------
 def decode(q, k_pool, v_pool, block_tables, context_lens, scale, softcap=0.0, window=0,
-           dtype="bf16"):
+           dtype="bf16", sink=0):
     """One new token per sequence attends over all ``L_b`` cached tokens of its
     sequence (the new token's own K/V included) through the block table.
 
@@ -163,7 +172,8 @@ def decode(q, k_pool, v_pool, block_tables, context_lens, scale, softcap=0.0, wi
         for g in range(Hkv):
             K, V = gather_sequence(k_pool, v_pool, block_tables[b], L, g, dtype)
             heads = slice(g * G, (g + 1) * G)
-            o, ls = attend(qv[b, heads], K, V, [L - 1] * G, scale, softcap, window, causal=True)
+            o, ls = attend(qv[b, heads], K, V, [L - 1] * G, scale, softcap, window, causal=True,
+                           sink=sink)
             out[b, heads] = o
             lse[b, heads] = ls
     return out, lse
@@ -355,4 +365,38 @@ def copy_blocks(src_ids, dst_ids, k_pool, v_pool):
         kp[d_] = k_pool[s_]
         vp[d_] = v_pool[s_]
     return kp, vp
+
+
+# ---------------------------------------------------------------------------
+# [inside] eviction statistics: H2O column mass of a decode step
+# ---------------------------------------------------------------------------
+def column_mass(q, k_pool, v_pool, block_tables, context_lens, scale, softcap=0.0, window=0,
+                dtype="bf16", sink=0, length=None):
+    """The attention each cached token receives from the decode query of its
+    sequence, summed over the query heads that share a kv head: ``mass[b, g,
+    t] = sum_{h in group g} p[b, h, t]`` with ``p`` the softmax weights of the
+    decode step ([inside]: the H2O eviction policy ranks tokens by the
+    attention they accumulate).  Invisible tokens get 0.  Returns float64
+    ``[B, Hkv, length]`` (``length`` defaults to the longest context)."""
+    qv = values(q, dtype)
+    B, Hq, D = qv.shape
+    Hkv = v_pool.shape[1]
+    G = Hq // Hkv
+    n_max = int(max(context_lens)) if len(context_lens) else 0
+    length = n_max if length is None else int(length)
+    mass = np.zeros((B, Hkv, length), dtype=np.float64)
+    for b in range(B):
+        L = int(context_lens[b])
+        if L == 0:
+            continue
+        keep = visible(L - 1, L, window, True, sink)
+        for g in range(Hkv):
+            K, _ = gather_sequence(k_pool, v_pool, block_tables[b], L, g, dtype)
+            s = scores(qv[b, g * G:(g + 1) * G], K, scale, softcap)   # [G, L]
+            s = np.where(keep, s, -np.inf)
+            m = s.max(axis=1, keepdims=True)
+            p = np.where(keep, np.exp(s - m), 0.0)
+            p /= p.sum(axis=1, keepdims=True)
+            mass[b, g, :L] = p.sum(axis=0)
+    return mass
 

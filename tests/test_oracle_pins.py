@@ -459,6 +459,76 @@ def test_p14_copy_blocks_rejects_ambiguous_pairs():
 
 
 # ---------------------------------------------------------------------------
+# P15 AttentionSink mask, P16 H2O column mass
+# ---------------------------------------------------------------------------
+def test_p15_sink_mask_brute_force():
+    for n in range(0, 40):
+        for W in (0, 1, 5, 16):
+            for S in (0, 1, 4, 20):
+                q = n - 1
+                keep = oracle.visible(q, n, W, True, S)
+                for t in range(n):
+                    want = t <= q and (W <= 0 or q - t < W or t < S)
+                    assert keep[t] == want, (n, W, S, t)
+
+
+@pytest.mark.parametrize("softcap", [0.0, 2.0])
+def test_p15_sink_decode_equals_loop_nest(softcap):
+    rng = np.random.default_rng(1500)
+    Hkv, G, D, L, W, S = 1, 2, 16, 50, 9, 4
+    K = rand_f32(rng, (Hkv, L, D), "f32")
+    V = rand_f32(rng, (Hkv, L, D), "f32")
+    q = rand_f32(rng, (1, G, D), "f32")
+    kp, vp, table = scatter_contiguous(K, V, "f32")
+    out, lse = oracle.decode(wl.to_bits(q, "f32"), kp, vp, table[None], np.array([L]), 0.3,
+                             softcap, W, "f32", sink=S)
+    for h in range(G):
+        ref, ref_lse = textbook(q[0, h], K[0], V[0], 0.3, softcap,
+                                lambda t: (L - 1 - t < W) or (t < S))
+        np.testing.assert_allclose(out[0, h], ref, rtol=1e-12, atol=1e-12)
+        assert abs(lse[0, h] - ref_lse) < 1e-12
+
+
+@pytest.mark.parametrize("window,sink", [(0, 0), (20, 0), (20, 5)])
+def test_p16_column_mass_sums_and_loop_nest(window, sink):
+    """Per kv head, a token's mass is the sum over its G query heads of the
+    softmax weight (textbook loop); the masses of one segment add up to G,
+    and invisible tokens get 0."""
+    case = wl.make_decode_case(1600 + window + sink, [1, 37, 70], 4, 2, 16, "f32", softcap=3.0)
+    mass = oracle.column_mass(case.q, case.k_pool, case.v_pool, case.block_tables,
+                              case.context_lens, case.scale, case.softcap, window, "f32", sink)
+    assert mass.shape == (3, 2, 70)
+    qv = f32vals(case.q, "f32")
+    for b, L in enumerate(case.context_lens.tolist()):
+        for g in range(2):
+            K, V = oracle.gather_sequence(case.k_pool, case.v_pool, case.block_tables[b], L, g,
+                                          "f32")
+            keep = (lambda t: L - 1 - t < window or t < sink) if window > 0 else (lambda t: True)
+            np.testing.assert_allclose(mass[b, g].sum(), 2.0, rtol=1e-12)
+            for t in range(70):
+                if t >= L or not keep(t):
+                    assert mass[b, g, t] == 0.0
+            # weight of token t for head h: the output of attention with one-hot V
+            for t in range(L):
+                if not keep(t):
+                    continue
+                onehot = np.zeros((L, 1))
+                onehot[t, 0] = 1.0
+                w = sum(textbook(qv[b, g * 2 + h], K, onehot, case.scale, case.softcap, keep)[0][0]
+                        for h in range(2))
+                assert abs(mass[b, g, t] - w) < 1e-12
+
+
+def test_p16_column_mass_uniform_when_q_is_zero():
+    case = wl.make_decode_case(1610, [45], 4, 1, 16, "bf16")
+    q0 = np.zeros_like(case.q)
+    mass = oracle.column_mass(q0, case.k_pool, case.v_pool, case.block_tables, case.context_lens,
+                              case.scale, 0.0, 16, "bf16", sink=3)
+    vis = [t for t in range(45) if 44 - t < 16 or t < 3]
+    np.testing.assert_allclose(mass[0, 0, vis], 4.0 / len(vis), rtol=1e-12)
+
+
+# ---------------------------------------------------------------------------
 # P10 append
 # ---------------------------------------------------------------------------
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
