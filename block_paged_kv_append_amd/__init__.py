@@ -49,6 +49,9 @@ SIGNATURES = {
     "paged_attn_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I,
                                                 _I, _I, _I, _I, _I, _F, _F, _I, _I, _P, _Z, _I,
                                                 _P]),
+    "paged_attn_decode_sink_h2o": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I,
+                                                  _I, _I, _I, _F, _F, _I, _I, _P, _P, _I, _P, _Z,
+                                                  _I, _P]),
     "paged_attn_prefill": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I,
                                           _I, _I, _I, _I, _F, _F, _I, _I, _P]),
     "pkv_decode_graph_create": (ctypes.c_int, [ctypes.POINTER(_P), _P, _P, _P, _P, _P, _P, _P,
@@ -344,6 +347,36 @@ def paged_attn_decode_append(out, q, k_new, v_new, k_pool, v_pool, block_tables,
                                       ws.numel() * ws.element_size(), _dtype_code(q),
                                       _stream(stream))
     _check("paged_attn_decode_append", rc)
+
+
+def paged_attn_decode_sink_h2o(out, q, k_pool, v_pool, block_tables, context_lens,
+                               max_context_len, scale, softcap=0.0, window=0, sink_tokens=0,
+                               scores=None, column_mass=None, lse=None, workspace=None,
+                               stream=None) -> None:
+    """Balanced decode with AttentionSink tokens beside the window and, when
+    ``column_mass [B, Hkv, S]`` is given (with ``scores [B, Hq, S]`` and
+    ``lse``), the H2O per-token attention mass of the step."""
+    nb, hkv, d, B, G, MB = _decode_dims(out, q, k_pool, v_pool, block_tables, context_lens)
+    stride = 0
+    if column_mass is not None:
+        if scores is None or lse is None:
+            raise ValueError("column_mass needs scores and lse")
+        stride = column_mass.shape[-1]
+        if tuple(column_mass.shape) != (B, hkv, stride) or \
+                tuple(scores.shape) != (B, hkv * G, stride):
+            raise ValueError("column_mass [B, Hkv, S] and scores [B, Hq, S] must agree")
+    need = paged_attn_decode_workspace_size(B, hkv, G, d, max_context_len, 0)
+    ws = workspace if workspace is not None else decode_workspace(need, q.device, stream)
+    lib = load_library()
+    rc = lib.paged_attn_decode_sink_h2o(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                        nb, _i32(block_tables, "block_tables"), MB,
+                                        _i32(context_lens, "context_lens"), int(max_context_len),
+                                        B, hkv, G, d, BLOCK_SIZE, float(scale), float(softcap),
+                                        int(window), int(sink_tokens), _ptr(scores),
+                                        _ptr(column_mass), int(stride), _ptr(ws),
+                                        ws.numel() * ws.element_size(), _dtype_code(q),
+                                        _stream(stream))
+    _check("paged_attn_decode_sink_h2o", rc)
 
 
 def decode_bucket(num_seqs: int) -> int:

@@ -97,17 +97,28 @@ int check_common(const char* fn, const void* out, const float* lse, const void* 
   return PKV_OK;
 }
 
-long long max_units_per_seq(int32_t max_context_len, int32_t window) {
+long long max_units_per_seq(int32_t max_context_len, int32_t window, int32_t sink) {
   long long n = (max_context_len + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
   if (window > 0) {
-    const long long w = (window + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE + 1;
+    const long long w = (window + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE + 1 +
+                        (sink + PKV_BLOCK_SIZE - 1) / PKV_BLOCK_SIZE;
     if (w < n) n = w;
   }
   return n;
 }
 
-int decode_impl(const char* fn, void* out, float* lse, const void* q, const void* k_new,
-                const void* v_new, const void* k_pool, const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
+// what a decode entry point adds to the plain decode
+struct DecodeExtras {
+  const void* k_new = nullptr;  // fused append
+  const void* v_new = nullptr;
+  int32_t sink = 0;             // AttentionSink tokens
+  float* scores = nullptr;      // H2O: per-head logits and column mass
+  float* column_mass = nullptr;
+  int32_t score_stride = 0;
+};
+
+int decode_impl(const char* fn, void* out, float* lse, const void* q, const DecodeExtras& x,
+                const void* k_pool, const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
                 int32_t max_blocks_per_seq, const int32_t* context_lens, int32_t max_context_len,
                 int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
                 int32_t block_size, float scale, float softcap, int32_t window,
@@ -117,7 +128,7 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
                         max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
                         gqa_group, head_dim, block_size, scale, softcap, dtype);
   if (rc != PKV_OK) return rc;
-  if ((k_new == nullptr) != (v_new == nullptr))
+  if ((x.k_new == nullptr) != (x.v_new == nullptr))
     return fail(PKV_EINVAL, "%s: k_new and v_new must both be given", fn);
   if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0)
     return fail(PKV_EUNSUPPORTED, "%s: partition_size %d is not a multiple of 16", fn,
@@ -138,8 +149,12 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
-  a.k_new = k_new;
-  a.v_new = v_new;
+  a.k_new = x.k_new;
+  a.v_new = x.v_new;
+  a.sink = x.sink;
+  a.scores = x.scores;
+  a.column_mass = x.column_mass;
+  a.score_stride = x.score_stride;
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.num_blocks = num_blocks;
@@ -175,7 +190,8 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const void
     rc = cu_count(&cus);
     if (rc != PKV_OK) return rc;
     a.cu_count = cus;
-    a.units_bound = (long long)num_seqs * num_kv_heads * max_units_per_seq(max_context_len, window);
+    a.units_bound =
+        (long long)num_seqs * num_kv_heads * max_units_per_seq(max_context_len, window, x.sink);
     a.part_blocks = 0;
     a.num_partitions = 0;
     a.num_workers = 0;  // chosen by launch_decode for the kernel variant
@@ -289,7 +305,7 @@ int paged_attn_decode(void* out, float* lse, const void* q, const void* k_pool,
                       int32_t gqa_group, int32_t head_dim, int32_t block_size, float scale,
                       float softcap, int32_t window, void* workspace, size_t workspace_bytes,
                       int32_t dtype, struct ihipStream_t* stream) {
-  return decode_impl("paged_attn_decode", out, lse, q, nullptr, nullptr, k_pool, v_pool,
+  return decode_impl("paged_attn_decode", out, lse, q, DecodeExtras{}, k_pool, v_pool,
                      num_blocks, block_tables,
                      max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
                      gqa_group, head_dim, block_size, scale, softcap, window, 0, workspace,
@@ -307,7 +323,7 @@ int paged_attn_decode_splitk(void* out, float* lse, const void* q, const void* k
   if (partition_size <= 0 || partition_size % PKV_BLOCK_SIZE != 0)
     return fail(PKV_EUNSUPPORTED, "paged_attn_decode_splitk: partition_size %d is not a positive "
                 "multiple of 16", partition_size);
-  return decode_impl("paged_attn_decode_splitk", out, lse, q, nullptr, nullptr, k_pool, v_pool,
+  return decode_impl("paged_attn_decode_splitk", out, lse, q, DecodeExtras{}, k_pool, v_pool,
                      num_blocks,
                      block_tables, max_blocks_per_seq, context_lens, max_context_len, num_seqs,
                      num_kv_heads, gqa_group, head_dim, block_size, scale, softcap, window,
@@ -328,10 +344,45 @@ int paged_attn_decode_append(void* out, float* lse, const void* q, const void* k
     return fail(PKV_EINVAL, "%s: k_new and v_new are required", fn);
   if (num_seqs > 0 && (!aligned(k_new, 16) || !aligned(v_new, 16)))
     return fail(PKV_EINVAL, "%s: k_new / v_new must be 16-byte aligned", fn);
-  return decode_impl(fn, out, lse, q, k_new, v_new, k_pool, v_pool, num_blocks, block_tables,
+  DecodeExtras x;
+  x.k_new = k_new;
+  x.v_new = v_new;
+  return decode_impl(fn, out, lse, q, x, k_pool, v_pool, num_blocks, block_tables,
                      max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
                      gqa_group, head_dim, block_size, scale, softcap, window, partition_size,
                      workspace, workspace_bytes, dtype, reinterpret_cast<hipStream_t>(stream));
+}
+
+int paged_attn_decode_sink_h2o(void* out, float* lse, const void* q, const void* k_pool,
+                               const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t max_context_len, int32_t num_seqs, int32_t num_kv_heads,
+                               int32_t gqa_group, int32_t head_dim, int32_t block_size,
+                               float scale, float softcap, int32_t window, int32_t sink_tokens,
+                               float* scores, float* column_mass, int32_t score_stride,
+                               void* workspace, size_t workspace_bytes, int32_t dtype,
+                               struct ihipStream_t* stream) {
+  const char* fn = "paged_attn_decode_sink_h2o";
+  if (sink_tokens < 0) return fail(PKV_EINVAL, "%s: sink_tokens %d", fn, sink_tokens);
+  if ((scores == nullptr) != (column_mass == nullptr))
+    return fail(PKV_EINVAL, "%s: scores and column_mass go together", fn);
+  if (column_mass != nullptr) {
+    if (lse == nullptr) return fail(PKV_EINVAL, "%s: column_mass needs lse", fn);
+    if (score_stride < max_context_len || score_stride % PKV_BLOCK_SIZE != 0)
+      return fail(PKV_EINVAL, "%s: score_stride %d: a multiple of 16 >= max_context_len %d", fn,
+                  score_stride, max_context_len);
+    if (!aligned(scores, 16) || !aligned(column_mass, 4))
+      return fail(PKV_EINVAL, "%s: scores must be 16-byte aligned, column_mass 4-byte", fn);
+  }
+  DecodeExtras x;
+  x.sink = window > 0 ? sink_tokens : 0;
+  x.scores = scores;
+  x.column_mass = column_mass;
+  x.score_stride = column_mass != nullptr ? score_stride : 0;
+  return decode_impl(fn, out, lse, q, x, k_pool, v_pool, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
+                     gqa_group, head_dim, block_size, scale, softcap, window, 0, workspace,
+                     workspace_bytes, dtype, reinterpret_cast<hipStream_t>(stream));
 }
 
 int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q_lens,

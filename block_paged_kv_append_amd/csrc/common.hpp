@@ -135,4 +135,33 @@ __device__ __forceinline__ SeqSpan seq_span(int L_raw, int window, int max_len) 
   return s;
 }
 
+// AttentionSink tokens kept beside a window: tokens [0, sink) stay visible,
+// and the walk visits the ns blocks holding them that lie before the
+// window's first block, then the window's blocks.  Walk index j is logical
+// block j < ns ? j : first_blk + j - ns.
+struct SinkPart {
+  int sink;  // visible sink tokens (0 without a window)
+  int ns;    // sink blocks walked before first_blk
+  __device__ __forceinline__ int blk(const SeqSpan& s, int j) const {
+    return j < ns ? j : j - ns + s.first_blk;
+  }
+  __device__ __forceinline__ bool visible(const SeqSpan& s, int t) const {
+    return (t < s.L) & ((t >= s.vis_lo) | (t < sink));
+  }
+};
+
+__device__ __forceinline__ SinkPart sink_part(const SeqSpan& s, int window, int sink) {
+  SinkPart k;
+  k.sink = (window > 0) ? min(max(sink, 0), s.L) : 0;
+  k.ns = min((k.sink + kBlock - 1) / kBlock, s.first_blk);
+  return k;
+}
+
+// the span of a sequence whose walk also covers its sink blocks
+__device__ __forceinline__ SeqSpan seq_span_sink(int L_raw, int window, int max_len, int sink) {
+  SeqSpan s = seq_span(L_raw, window, max_len);
+  if (s.L > 0) s.nb += sink_part(s, window, sink).ns;
+  return s;
+}
+
 }  // namespace pkv

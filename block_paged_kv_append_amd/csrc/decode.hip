@@ -42,14 +42,16 @@
 #include "attn_tile.hpp"
 #include "launch.hpp"
 
-// bf16: blocks streamed through per-wave LDS rings (1) or registers (0) at
-// head_dim 256 (the ring holds two 16 KiB blocks per wave there; at smaller
-// head_dim the register form keeps two workgroups per CU and is faster)
-#ifndef PKV_DECODE_RING
-#define PKV_DECODE_RING 1
+// bf16: blocks streamed through per-wave LDS rings at every head_dim (32 KiB
+// per wave: 2, 4 or 8 blocks in flight at head_dim 256, 128, 64).  The
+// register form (blocks loaded into registers, two workgroups per CU) is kept
+// switched off: runs of its head_dim 64 / 128 instantiations gave wrong
+// results and memory faults whose cause was not found.
+#ifndef PKV_DECODE_REGISTER_FORM
+#define PKV_DECODE_REGISTER_FORM 0
 #endif
 template <int D>
-constexpr bool kRingForm = PKV_DECODE_RING && D >= 256;
+constexpr bool kRingForm = !PKV_DECODE_REGISTER_FORM;
 
 namespace pkv {
 namespace {
@@ -218,7 +220,7 @@ __device__ __forceinline__ void finalize_vec(const DecodeArgs& a, int b, int h_g
 // group + kGroups, ... for dims 4 lane .. 4 lane + 3; it issues the loads of
 // up to kPer slots at once, then folds them into a running (max, sum,
 // output); the groups are folded through LDS at the end.
-template <bool BF16, int D, typename SlotList>
+template <bool BF16, int D, typename SlotList, bool V = false>
 __device__ void merge_row(const DecodeArgs& a, int b, int g, int h, SlotList slots, float* lds) {
   constexpr int kLanes = D / 4;                 // float4 columns per row
   constexpr int kGroups = kThreads / kLanes;    // slot groups (16, 8 or 4)
@@ -325,7 +327,7 @@ struct BalancedSlots {
 // The four waves' (max, sum, output) of one piece, in LDS as lo[wave][head][D]
 // and lml[wave][head][2]: merged, then written as the output (whole segment)
 // or as the piece's partial.
-template <bool BF16, int D>
+template <bool BF16, int D, bool V = false>
 __device__ void combine_waves(const DecodeArgs& a, const Piece& pc, const float* lo, const float* lml) {
   const int G = a.gqa_group;
   const int b = pc.b, g = pc.g;
@@ -364,8 +366,18 @@ __device__ void combine_waves(const DecodeArgs& a, const Piece& pc, const float*
 
 }
 
+// One block's logits of query row h for this lane's tokens tok .. tok + 3
+// (base-2 logits s2, -inf where not visible), stored in natural-log units.
+__device__ __forceinline__ void put_scores(const DecodeArgs& a, int b, int h, bool row_ok, int tok,
+                                           const float (&s2)[4]) {
+  if (!row_ok) return;
+  const int Hq = a.num_kv_heads * a.gqa_group;
+  float* dst = a.scores + ((size_t)b * Hq + h) * a.score_stride + tok;
+  *reinterpret_cast<f32x4*>(dst) = f32x4{s2[0] * kLn2, s2[1] * kLn2, s2[2] * kLn2, s2[3] * kLn2};
+}
+
 // One piece: all four waves of the workgroup.
-template <bool BF16, int D, bool FUSE>
+template <bool BF16, int D, bool FUSE, bool EVICT>
 __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece& pc, float* lds) {
   using T = typename Elem<BF16>::T;
   using KV = KVFrag<BF16, D>;
@@ -389,7 +401,10 @@ __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece
   for (int t = 0; t < NT; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
 
-  const int* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk;
+  // walk index j -> logical block (sink blocks first in the eviction variant)
+  const SinkPart sk = EVICT ? sink_part(sp, a.window, a.sink) : SinkPart{0, 0};
+  const int* bt = EVICT ? a.block_tables + (size_t)b * a.max_blocks_per_seq
+                       : a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk;
   const T* kpool = reinterpret_cast<const T*>(a.k_pool);
   const T* vpool = reinterpret_cast<const T*>(a.v_pool);
   constexpr size_t kTile = (size_t)D * kBlock;
@@ -425,7 +440,8 @@ __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece
 
   auto body = [&](int i, auto prefetch) {
     constexpr bool PF = decltype(prefetch)::value;
-    const int tok0 = (sp.first_blk + pc.j0 + wave + kWaves * i) * kBlock;
+    const int tok0 = (EVICT ? sk.blk(sp, pc.j0 + wave + kWaves * i)
+                            : sp.first_blk + pc.j0 + wave + kWaves * i) * kBlock;
     if constexpr (FUSE) {
       if (nt.own && i == nw - 1) {
         nt.put_k(buf.k, lane);
@@ -444,9 +460,14 @@ __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = tok0 + 4 * j + r;
-      const bool vis = ok & (t >= sp.vis_lo) & (t < sp.L);
+      bool vis;
+      if constexpr (EVICT)
+        vis = ok & sk.visible(sp, t);
+      else
+        vis = ok & (t >= sp.vis_lo) & (t < sp.L);
       s2[r] = vis ? xf(sc[r]) : kNegInf;
     }
+    if constexpr (EVICT) put_scores(a, b, g * G + c, c < G, tok0 + 4 * j, s2);
     float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
@@ -486,7 +507,10 @@ __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece
 
   for (int base = 0; base < nw; base += 64) {
     const int cnt = min(64, nw - base);
-    tbl = lane < cnt ? bt[pc.j0 + wave + kWaves * (base + lane)] : 0;
+    if constexpr (EVICT)
+      tbl = lane < cnt ? bt[sk.blk(sp, pc.j0 + wave + kWaves * (base + lane))] : 0;
+    else
+      tbl = lane < cnt ? bt[pc.j0 + wave + kWaves * (base + lane)] : 0;
     if constexpr (kPrefetch<BF16, D>) {
       off = tile(0, ok);
       buf.load(kpool + off, vpool + off, lane);
@@ -522,7 +546,7 @@ __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece
   }
   __syncthreads();
 
-  combine_waves<BF16, D>(a, pc, lo, lml);
+  combine_waves<BF16, D, EVICT>(a, pc, lo, lml);
   __syncthreads();  // LDS is reused by the next piece
 }
 
@@ -546,7 +570,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_range(const void* base, i
 // are buffer loads with a per-block byte range, empty for a block that may not
 // be read, so they are unconditional.  The query fragments and the output
 // accumulators live in the accumulator file.
-template <int D, bool FUSE>
+template <int D, bool FUSE, bool EVICT>
 __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const Piece& pc,
                                float* lds) {
   constexpr int KS = D / 32;  // score products
@@ -565,6 +589,7 @@ __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const 
   sp.nb = __builtin_amdgcn_readfirstlane(pc.sp.nb);
   sp.vis_lo = __builtin_amdgcn_readfirstlane(pc.sp.vis_lo);
   sp.L = __builtin_amdgcn_readfirstlane(pc.sp.L);
+  const SinkPart sk = EVICT ? sink_part(sp, a.window, a.sink) : SinkPart{0, 0};
 
   u32x4 qf[KS];
   {
@@ -585,18 +610,21 @@ __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const 
 
   const int span = j1 - j0 - wave;
   const int nw = span > 0 ? (span + kWaves - 1) / kWaves : 0;
-  const int* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk + j0 + wave;
+  const int* bt = EVICT ? a.block_tables + (size_t)b * a.max_blocks_per_seq
+                       : a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk + j0 + wave;
+  // table entry of this wave's block idx
+  auto tbl_at = [&](int idx) { return EVICT ? bt[sk.blk(sp, j0 + wave + kWaves * idx)] : bt[kWaves * idx]; };
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
   NewToken<2, D> nt;
   if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
   // this wave's table entries, 64 at a time (lane l: block tbase + l)
   int tbase = 0;
-  int tbl = lane < nw ? bt[kWaves * lane] : 0;
+  int tbl = lane < nw ? tbl_at(lane) : 0;
   auto ranges = [&](int i, bool& ok, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv) {
     if (i - tbase >= 64) {  // uniform, every 64 blocks
       tbase += 64;
-      tbl = tbase + lane < nw ? bt[kWaves * (tbase + lane)] : 0;
+      tbl = tbase + lane < nw ? tbl_at(tbase + lane) : 0;
     }
     const int phys = __builtin_amdgcn_readlane(tbl, (i - tbase) & 63);
     ok = i < nw && (unsigned)phys < (unsigned)a.num_blocks;
@@ -625,7 +653,8 @@ __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const 
     load_k(rk);
     load_v(rv);
     for (int i = 0; i < nw; ++i) {
-      const int tok0 = (sp.first_blk + j0 + wave + kWaves * i) * kBlock;
+      const int tok0 =
+          (EVICT ? sk.blk(sp, j0 + wave + kWaves * i) : sp.first_blk + j0 + wave + kWaves * i) * kBlock;
       if constexpr (FUSE) {
         if (nt.own && i == nw - 1) {
           nt.put_k(kb, lane);
@@ -646,9 +675,14 @@ __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const 
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = tok0 + 4 * j + r;
-        const bool vis = ok & (t >= sp.vis_lo) & (t < sp.L);
+        bool vis;
+        if constexpr (EVICT)
+          vis = ok & sk.visible(sp, t);
+        else
+          vis = ok & (t >= sp.vis_lo) & (t < sp.L);
         s2[r] = vis ? xf(acc[r]) : kNegInf;
       }
+      if constexpr (EVICT) put_scores(a, b, g * G + c, c < G, tok0 + 4 * j, s2);
       float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
       mx = quad_max(mx);  // over the 16 tokens: lanes c, c + 16, c + 32, c + 48
       if (__any(mx > m_run + kLazy)) {
@@ -695,7 +729,7 @@ __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const 
     }
   }
   __syncthreads();
-  combine_waves<true, D>(a, pc, lo, lml);
+  combine_waves<true, D, EVICT>(a, pc, lo, lml);
   __syncthreads();  // LDS is reused by the next piece
 }
 
@@ -709,7 +743,7 @@ constexpr int kRingBytesPerWave = 32768;
 // vector registers held by loads and no barrier in the loop.  A block is
 // copied verbatim (its K tile, then its V tile, 1 KiB per copy), so the
 // operands are read with the pool's own layouts.
-template <int D, bool FUSE>
+template <int D, bool FUSE, bool EVICT>
 __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const Piece& pc,
                                float* lds) {
   constexpr int KS = D / 32;                        // score products
@@ -729,6 +763,7 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   sp.nb = __builtin_amdgcn_readfirstlane(pc.sp.nb);
   sp.vis_lo = __builtin_amdgcn_readfirstlane(pc.sp.vis_lo);
   sp.L = __builtin_amdgcn_readfirstlane(pc.sp.L);
+  const SinkPart sk = EVICT ? sink_part(sp, a.window, a.sink) : SinkPart{0, 0};
 
   u32x4 qf[KS];
   {
@@ -747,7 +782,10 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
 
   const int span = j1 - j0 - wave;
   const int nw = span > 0 ? (span + kWaves - 1) / kWaves : 0;
-  const int* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk + j0 + wave;
+  const int* bt = EVICT ? a.block_tables + (size_t)b * a.max_blocks_per_seq
+                       : a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk + j0 + wave;
+  // table entry of this wave's block idx
+  auto tbl_at = [&](int idx) { return EVICT ? bt[sk.blk(sp, j0 + wave + kWaves * idx)] : bt[kWaves * idx]; };
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
   char* ring = reinterpret_cast<char*>(lds) + wave * kRingBytesPerWave;
@@ -755,14 +793,14 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
   // this wave's table entries, 64 at a time (lane l: block tbase + l)
   int tbase = 0;
-  int tbl = lane < nw ? bt[kWaves * lane] : 0;
+  int tbl = lane < nw ? tbl_at(lane) : 0;
   uint32_t okbits = 0;  // bit (block % NS): that slot's block was readable
 
   // copy this wave's block i (past the end: an empty range, zeros) into its slot
   auto issue = [&](int i) {
     if (i - tbase >= 64) {  // uniform, every 64 blocks
       tbase += 64;
-      tbl = tbase + lane < nw ? bt[kWaves * (tbase + lane)] : 0;
+      tbl = tbase + lane < nw ? tbl_at(tbase + lane) : 0;
     }
     const int phys = __builtin_amdgcn_readlane(tbl, (i - tbase) & 63);
     const bool ok = i < nw && (unsigned)phys < (unsigned)a.num_blocks;
@@ -793,7 +831,8 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
     const bool ok = (okbits >> slot) & 1u;
     const char* kt = ring + slot * 2 * kTileBytes;
     const char* vt = kt + kTileBytes;
-    const int tok0 = (sp.first_blk + j0 + wave + kWaves * i) * kBlock;
+    const int tok0 =
+        (EVICT ? sk.blk(sp, j0 + wave + kWaves * i) : sp.first_blk + j0 + wave + kWaves * i) * kBlock;
 
     u32x4 kf[KS];
 #pragma unroll
@@ -820,9 +859,14 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = tok0 + 4 * j + r;
-      const bool vis = ok & (t >= sp.vis_lo) & (t < sp.L);
+      bool vis;
+      if constexpr (EVICT)
+        vis = ok & sk.visible(sp, t);
+      else
+        vis = ok & (t >= sp.vis_lo) & (t < sp.L);
       s2[r] = vis ? xf(acc[r]) : kNegInf;
     }
+    if constexpr (EVICT) put_scores(a, b, g * G + c, c < G, tok0 + 4 * j, s2);
     float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
     mx = quad_max(mx);
     if (__any(mx > m_run + kLazy)) {
@@ -869,12 +913,12 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
     }
   }
   __syncthreads();
-  combine_waves<true, D>(a, pc, lo, lml);
+  combine_waves<true, D, EVICT>(a, pc, lo, lml);
   __syncthreads();  // LDS is reused by the next piece
 }
 
 // Output of a sequence with nothing to attend to: 0, lse = -inf.
-template <bool BF16, int D>
+template <bool BF16, int D, bool V = false>
 __device__ void write_empty(const DecodeArgs& a, int b, int h_lo, int h_hi) {
   using T = typename Elem<BF16>::T;
   const int Hq = a.num_kv_heads * a.gqa_group;
@@ -889,7 +933,7 @@ __device__ void write_empty(const DecodeArgs& a, int b, int h_lo, int h_hi) {
 // A piece of a split segment has stored its partial: count it in; the
 // workgroup that counts the last piece merges all of them into the output
 // and resets the counter (the counters start at zero and are left at zero).
-template <bool BF16, int D, typename SlotList>
+template <bool BF16, int D, bool V, typename SlotList>
 __device__ void finish_split(const DecodeArgs& a, int b, int g, SlotList slots, float* lds) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are done
   __syncthreads();
@@ -901,26 +945,33 @@ __device__ void finish_split(const DecodeArgs& a, int b, int g, SlotList slots, 
   const bool last = flag[0] != 0;
   __syncthreads();  // LDS is reused below
   if (!last) return;
-  for (int h = 0; h < a.gqa_group; ++h) merge_row<BF16, D>(a, b, g, h, slots, lds);
+  for (int h = 0; h < a.gqa_group; ++h) merge_row<BF16, D, SlotList, V>(a, b, g, h, slots, lds);
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
 }
 
-template <bool BF16, int D, bool FIXED, bool FUSE>
+template <bool BF16, int D, bool FIXED, bool FUSE, bool EVICT>
 __global__ __launch_bounds__(kThreads, (BF16 && !kRingForm<D>) ? 2 : 1) void decode_kernel(DecodeArgs a) {
   extern __shared__ float lds[];
   auto run_one = [&](const LogitXform& xf, const Piece& pc) {
     if constexpr (BF16) {
       if constexpr (kRingForm<D>)
-        run_piece_ring<D, FUSE>(a, xf, pc, lds);
+        run_piece_ring<D, FUSE, EVICT>(a, xf, pc, lds);
       else
-        run_piece_bf16<D, FUSE>(a, xf, pc, lds);
+        run_piece_bf16<D, FUSE, EVICT>(a, xf, pc, lds);
     } else {
-      run_piece<BF16, D, FUSE>(a, xf, pc, lds);
+      run_piece<BF16, D, FUSE, EVICT>(a, xf, pc, lds);
     }
   };
   const LogitXform xf = make_xform(a.scale, a.softcap);
   const int Hkv = a.num_kv_heads, G = a.gqa_group;
+  // a sequence's visible span (with the sink tokens in the eviction variant)
+  auto span = [&](int L_raw) {
+    if constexpr (EVICT)
+      return seq_span_sink(L_raw, a.window, a.max_context_len, a.sink);
+    else
+      return seq_span(L_raw, a.window, a.max_context_len);
+  };
 
   if constexpr (FIXED) {
     const int NP = a.num_partitions, PB = a.part_blocks;
@@ -931,7 +982,7 @@ __global__ __launch_bounds__(kThreads, (BF16 && !kRingForm<D>) ? 2 : 1) void dec
     pc.g = g;
     pc.sp = seq_span(a.context_lens[b], a.window, a.max_context_len);
     if (pc.sp.nb == 0) {
-      if (p == 0) write_empty<BF16, D>(a, b, g * G, (g + 1) * G);
+      if (p == 0) write_empty<BF16, D, EVICT>(a, b, g * G, (g + 1) * G);
       return;
     }
     const int last_blk = pc.sp.first_blk + pc.sp.nb - 1;
@@ -944,7 +995,7 @@ __global__ __launch_bounds__(kThreads, (BF16 && !kRingForm<D>) ? 2 : 1) void dec
     run_one(xf, pc);
     if (!(pc.j0 == 0 && pc.j1 == pc.sp.nb)) {
       const int p_lo = pc.sp.first_blk / PB, p_hi = last_blk / PB;
-      finish_split<BF16, D>(a, b, g, SplitSlots{seg * NP, p_lo, p_hi}, lds);
+      finish_split<BF16, D, EVICT>(a, b, g, SplitSlots{seg * NP, p_lo, p_hi}, lds);
     }
   } else {
     const int N = a.num_workers, w = blockIdx.x;
@@ -953,15 +1004,15 @@ __global__ __launch_bounds__(kThreads, (BF16 && !kRingForm<D>) ? 2 : 1) void dec
 
     // sequences with no visible token
     for (int b = w; b < B; b += N) {
-      if (seq_span(a.context_lens[b], a.window, a.max_context_len).nb == 0)
-        write_empty<BF16, D>(a, b, 0, Hkv * G);
+      if (span(a.context_lens[b]).nb == 0)
+        write_empty<BF16, D, EVICT>(a, b, 0, Hkv * G);
     }
 
     // total units W (every wave computes the same value)
     long long W = 0;
     for (int base = 0; base < B; base += kWave) {
       const int b = base + lane;
-      const int nb = b < B ? seq_span(a.context_lens[b], a.window, a.max_context_len).nb : 0;
+      const int nb = b < B ? span(a.context_lens[b]).nb : 0;
       W += wave_sum_i64(nb);
     }
     W *= Hkv;
@@ -974,7 +1025,7 @@ __global__ __launch_bounds__(kThreads, (BF16 && !kRingForm<D>) ? 2 : 1) void dec
     for (int base = 0; base < B; base += kWave) {
       const int b = base + lane;
       const long long nbh =
-          b < B ? (long long)seq_span(a.context_lens[b], a.window, a.max_context_len).nb * Hkv
+          b < B ? (long long)span(a.context_lens[b]).nb * Hkv
                 : 0;
       const long long incl = wave_incl_scan_i64(nbh, lane);
       const unsigned long long hit = __ballot(run + incl > a0);
@@ -989,7 +1040,7 @@ __global__ __launch_bounds__(kThreads, (BF16 && !kRingForm<D>) ? 2 : 1) void dec
 
     Piece pc;
     pc.b = b0;
-    pc.sp = seq_span(a.context_lens[b0], a.window, a.max_context_len);
+    pc.sp = span(a.context_lens[b0]);
     pc.g = (int)((a0 - seg_base) / pc.sp.nb);
     pc.S = seg_base + (long long)pc.g * pc.sp.nb;
     long long pos = a0;
@@ -1001,7 +1052,7 @@ __global__ __launch_bounds__(kThreads, (BF16 && !kRingForm<D>) ? 2 : 1) void dec
       pc.slot = first ? 2 * w : 2 * w + 1;
       run_one(xf, pc);
       if (!(pc.j0 == 0 && pc.j1 == pc.sp.nb))
-        finish_split<BF16, D>(a, pc.b, pc.g, BalancedSlots{W, pc.S, E, N}, lds);
+        finish_split<BF16, D, EVICT>(a, pc.b, pc.g, BalancedSlots{W, pc.S, E, N}, lds);
       first = false;
       pos = E;
       pc.S = E;
@@ -1010,11 +1061,30 @@ __global__ __launch_bounds__(kThreads, (BF16 && !kRingForm<D>) ? 2 : 1) void dec
         pc.g = 0;
         do {
           if (++pc.b >= B) return;
-          pc.sp = seq_span(a.context_lens[pc.b], a.window, a.max_context_len);
+          pc.sp = span(a.context_lens[pc.b]);
         } while (pc.sp.nb == 0);
       }
     }
   }
+}
+
+// H2O statistic of the decode step: mass[b, g, t] = sum over the group's
+// query heads h of exp(logit[b, h, t] - lse[b, h]), the softmax weight of
+// token t, for visible t; 0 elsewhere in the row.  One thread per token.
+__global__ __launch_bounds__(kThreads) void column_mass_kernel(DecodeArgs a) {
+  const int t = blockIdx.x * kThreads + threadIdx.x;
+  if (t >= a.score_stride) return;
+  const int seg = blockIdx.y, Hkv = a.num_kv_heads, G = a.gqa_group;
+  const int b = seg / Hkv, g = seg % Hkv;
+  const SeqSpan sp = seq_span(a.context_lens[b], a.window, a.max_context_len);
+  const SinkPart sk = sink_part(sp, a.window, a.sink);
+  float mass = 0.f;
+  if (sk.visible(sp, t)) {
+    const size_t row0 = (size_t)b * Hkv * G + (size_t)g * G;
+    for (int h = 0; h < G; ++h)
+      mass += fast_exp2((a.scores[(row0 + h) * a.score_stride + t] - a.lse[row0 + h]) * kLog2e);
+  }
+  a.column_mass[(size_t)seg * a.score_stride + t] = mass;
 }
 
 // The combine buffer holds the four waves' partial outputs: up to 66 KiB for
@@ -1059,10 +1129,17 @@ hipError_t launch_d(DecodeArgs a, hipStream_t stream) {
   lds = std::max(lds, (size_t)(4 * kThreads + 2 * 16) * sizeof(float));  // a merge
   if (BF16 && kRingForm<D>) lds = std::max(lds, (size_t)kWaves * kRingBytesPerWave);
   if (a.part_blocks > 0)
-    return a.k_new ? launch_k(decode_kernel<BF16, D, true, true>, a, lds, stream)
-                   : launch_k(decode_kernel<BF16, D, true, false>, a, lds, stream);
-  return a.k_new ? launch_k(decode_kernel<BF16, D, false, true>, a, lds, stream)
-                 : launch_k(decode_kernel<BF16, D, false, false>, a, lds, stream);
+    return a.k_new ? launch_k(decode_kernel<BF16, D, true, true, false>, a, lds, stream)
+                   : launch_k(decode_kernel<BF16, D, true, false, false>, a, lds, stream);
+  if (a.scores) {  // balanced split with per-head logits, then the column mass
+    hipError_t e = launch_k(decode_kernel<BF16, D, false, false, true>, a, lds, stream);
+    if (e != hipSuccess || a.column_mass == nullptr) return e;
+    const dim3 grid((a.score_stride + kThreads - 1) / kThreads, a.num_seqs * a.num_kv_heads);
+    column_mass_kernel<<<grid, kThreads, 0, stream>>>(a);
+    return hipGetLastError();
+  }
+  return a.k_new ? launch_k(decode_kernel<BF16, D, false, true, false>, a, lds, stream)
+                 : launch_k(decode_kernel<BF16, D, false, false, false>, a, lds, stream);
 }
 
 template <bool BF16>

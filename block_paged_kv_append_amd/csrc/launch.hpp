@@ -62,6 +62,14 @@ struct DecodeArgs {
   int32_t num_workers;      // grid size (set by launch_decode in balanced mode)
   int32_t part_blocks;      // 0: balanced split of all blocks; > 0: fixed partitions of this many blocks
   int32_t num_partitions;   // fixed partitions per sequence
+  // eviction-policy variant (balanced split only): tokens [0, sink) stay
+  // visible beside the window; optional per-head logits
+  // [num_seqs, num_q_heads, score_stride] (natural log, -inf where not
+  // visible) and per-kv-head attention mass [num_seqs, num_kv_heads, score_stride]
+  int32_t sink;
+  int32_t score_stride;
+  float* scores;
+  float* column_mass;
 };
 
 struct PrefillArgs {

@@ -256,6 +256,39 @@ int paged_attn_decode_append(void* out, float* lse, const void* q, const void* k
                              size_t workspace_bytes, int32_t dtype, struct ihipStream_t* stream);
 
 /*
+ * paged_attn_decode_sink_h2o -- the decode variants behind two of the
+ * engine's eviction policies, AttentionSink and H2O (page "Inference
+ * Server", GitHub README, section "What's inside"), on the balanced split of
+ * paged_attn_decode.  Arguments as paged_attn_decode, plus
+ *   sink_tokens   with window > 0, tokens [0, sink_tokens) stay visible
+ *                 beside the window (the attention sinks); 0: plain window.
+ *                 Ignored without a window (every token is visible then).
+ *   scores        NULL, or fp32 [num_seqs, num_q_heads, score_stride],
+ *                 16-byte aligned: receives the natural-log logits of every
+ *                 token of the blocks the decode reads (-inf where not
+ *                 visible); other entries are left alone
+ *   column_mass   NULL, or fp32 [num_seqs, num_kv_heads, score_stride]:
+ *                 mass[b, g, t] = sum over the group's query heads h of the
+ *                 softmax weight of token t, exp(logit - lse); 0 for tokens
+ *                 not visible (the whole row is written).  Needs scores and
+ *                 lse.
+ *   score_stride  a multiple of 16, >= max_context_len (when column_mass)
+ * Errors as paged_attn_decode; PKV_EINVAL for a negative sink_tokens,
+ * scores without column_mass (or the reverse), column_mass without lse, or a
+ * bad score_stride / alignment.  With column_mass, two kernels run (the
+ * decode writes logits and lse, a second one forms the mass).
+ */
+int paged_attn_decode_sink_h2o(void* out, float* lse, const void* q, const void* k_pool,
+                               const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
+                               int32_t max_blocks_per_seq, const int32_t* context_lens,
+                               int32_t max_context_len, int32_t num_seqs, int32_t num_kv_heads,
+                               int32_t gqa_group, int32_t head_dim, int32_t block_size,
+                               float scale, float softcap, int32_t window, int32_t sink_tokens,
+                               float* scores, float* column_mass, int32_t score_stride,
+                               void* workspace, size_t workspace_bytes, int32_t dtype,
+                               struct ihipStream_t* stream);
+
+/*
  * pkv_decode_graph -- a decode tick (paged_attn_decode_append) captured once
  * into a HIP graph for one batch-size bucket and replayed every tick: the
  * engine replays decode steps captured per batch-size bucket (page

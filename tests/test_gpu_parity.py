@@ -281,3 +281,23 @@ def test_prefill_single_row_equals_decode():
     torch.cuda.synchronize()
     d = np.abs(out - dout.float().cpu().numpy())
     assert d.max() <= 2e-2
+
+# ---------------------------------------------------------------------------
+# mixed batch: decode rows (1-row chunks) and prefill chunks in one launch
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("D,cap,W", [(128, 0.0, 0), (256, 50.0, 0), (256, 0.0, 300)])
+def test_mixed_batch_decode_rows_and_chunks(D, cap, W):
+    """One prefill launch over a ragged batch mixing one-row chunks (decode
+    rows) with multi-row chunks, against the oracle."""
+    cached = [100, 700, 31, 2000, 64, 5, 1500]
+    chunk = [1, 300, 1, 1, 64, 1, 1]
+    case = wl.make_prefill_case(480 + D + W, cached, chunk, 8, 2, D, "bf16", softcap=cap, window=W)
+    banner("mixed batch", D, cap, W)
+    kp, vp = run_append(case)
+    out, lse = run_prefill(case, kp, vp)
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           "bf16")
+    ref, ref_lse = oracle.prefill(case.q, case.cu_q_lens, kr, vr, case.block_tables,
+                                  case.context_lens, case.scale, case.softcap, case.window, "bf16")
+    check_close(out, ref, "bf16", "mixed batch")
+    check_lse(lse, ref_lse, "mixed batch")
