@@ -81,8 +81,8 @@ enum pkv_status {
 
 /*
  * paged_kv_append -- write new K/V rows into their cache slots.
- * "Block-paged KV cache" (page "Inference Server", section "The engine"): the
- * K/V of every new token is copied into the slot the host reserved for it;
+ * The KV cache is paged in fixed-size blocks (page "Inference Server", section
+ * "The engine"): the K/V of every new token is copied into the slot the host reserved for it;
  * a chunk of a long prompt is appended this way before it attends (chunked
  * prefill, page "Inference Server -- Architecture Map", section "How a single
  * request flows through the system"), and so is each decode token.
@@ -174,8 +174,8 @@ size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
 
 /*
  * paged_attn_decode -- batched one-token decode over the block-paged cache.
- * "Paged decode kernel reading K/V through block tables" (page "Inference
- * Server", section "The engine"); one batched decode per tick over every
+ * The engine's decode kernel reads K/V through per-sequence block tables (page
+ * "Inference Server", section "The engine"); one batched decode per tick over every
  * active request (page "Inference Server -- Architecture Map", section "How a
  * single request flows through the system").
  *
@@ -326,8 +326,8 @@ void pkv_decode_graph_destroy(pkv_decode_graph* graph);
 /*
  * paged_attn_prefill -- causal attention of a chunk of new tokens over the
  * cached prefix plus the chunk (chunked / batched prefill, page "Inference
- * Server", section "The engine"; "Triton paged ... prefill kernels reading
- * K/V through block tables").  The chunk's K/V must already be in the pool
+ * Server", section "The engine", where the prefill kernels also read K/V
+ * through the block tables).  The chunk's K/V must already be in the pool
  * (paged_kv_append); prefix blocks may be shared between sequences.
  *
  *   out           [num_q_tokens, num_q_heads, head_dim]

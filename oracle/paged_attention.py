@@ -21,7 +21,8 @@ Sources are three web pages about one single-GPU inference engine:
   tick; every tick runs one batched decode over all active requests, one new
   token each.
 
-The first read path the pages describe is "gather, then SDPA" [inside]; this
+The first read path the pages describe gathers the K/V rows and then runs
+standard attention on them [inside]; this
 oracle has exactly that structure: gather a sequence's K/V rows through its
 block table into contiguous arrays, then apply the textbook definition
 softmax(scale * q k^T) v over the visible keys.  Everything is evaluated in

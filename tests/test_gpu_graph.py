@@ -1,6 +1,6 @@
 """HIP graph capture of the library's launches (the pages' engine replays a
-captured decode step; page "Inference Server", section "The engine": bucketed
-CUDA-graph decode).  Every replay, with eager work and synchronisation between
+captured decode step, one capture per batch-size bucket; page "Inference
+Server", section "The engine").  Every replay, with eager work and synchronisation between
 replays, must reproduce the eager result bit for bit."""
 import numpy as np
 import pytest
