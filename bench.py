@@ -352,6 +352,58 @@ def time_copy_blocks(bench, iters, torch):
     return ms, n, 2 * n * per_pair  # bytes read + written
 
 
+def time_mixed(torch, pkv, wl, iters=20):
+    """A mixed batch: 4 prefill chunks (2048 cached + 512 new tokens) and 28
+    decode rows (contexts uniform in [512, 4096]), 8 q / 2 kv heads, D 256,
+    bf16.  Times paged_attn_mixed (chunks through the prefill kernel, decode
+    rows through the balanced decode split) and, for comparison, the same
+    batch through one prefill launch."""
+    import numpy as np
+
+    rng = np.random.default_rng(6)
+    lens = rng.integers(512, 4097, size=28)
+    cached = [2048] * 4 + [int(L) - 1 for L in lens]
+    chunk = [512] * 4 + [1] * 28
+    c = wl.make_prefill_case(6, cached, chunk, 8, 2, 256, "bf16", scale=1.0 / 16.0, softcap=50.0)
+    kp, vp = pkv.from_bits(c.k_pool, "bf16"), pkv.from_bits(c.v_pool, "bf16")
+    pkv.paged_kv_append(pkv.from_bits(c.k_new, "bf16"), pkv.from_bits(c.v_new, "bf16"),
+                        torch.from_numpy(c.slot_mapping).cuda(), kp, vp)
+    q = pkv.from_bits(c.q, "bf16")
+    out = torch.empty_like(q)
+    cu_all = torch.from_numpy(c.cu_q_lens).cuda()
+    cu4 = torch.from_numpy(c.cu_q_lens[:5].copy()).cuda()
+    bt = torch.from_numpy(c.block_tables).cuda()
+    cl = torch.from_numpy(c.context_lens).cuda()
+    ws = torch.zeros(pkv.paged_attn_decode_workspace_size(28, 2, 4, 256, c.max_context_len, 0),
+                     dtype=torch.uint8, device="cuda")
+
+    def mixed():
+        for _ in range(4):
+            pkv.paged_attn_mixed(out, q, cu4, 2048, 512, kp, vp, bt, cl, c.max_context_len,
+                                 c.scale, c.softcap, 0, workspace=ws)
+
+    def one_prefill():
+        for _ in range(4):
+            pkv.paged_attn_prefill(out, q, cu_all, 512, kp, vp, bt, cl, c.max_context_len,
+                                   c.scale, c.softcap, 0)
+
+    res = []
+    for fn in (mixed, one_prefill):
+        fn()
+        torch.cuda.synchronize()
+        g = capture(torch, fn)
+        warm(g, torch, 0.2)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(iters)]
+        for i in range(iters):
+            ev[i][0].record()
+            g.replay()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        res.append(float(np.mean([a.elapsed_time(b) for a, b in ev])) / 4)
+    return res[0], res[1]
+
+
 def copy_rate(torch) -> float:
     """GB/s (bytes read + written) of a plain 1 GiB device copy right now: the
     bandwidth this GPU delivers to a trivial kernel, as context for the rates
@@ -511,6 +563,11 @@ def main():
         line["copy_blocks"] = {"pairs": cb_pairs, "ms": round(cb_ms, 5),
                                "gbs": round(cb_bytes / (cb_ms * 1e-3) / 1e9, 1), "bytes": cb_bytes,
                                "pool": "gemma_decode (2 kv heads, D256, bf16: 32 KiB per pair)"}
+        mx_ms, one_ms = time_mixed(torch, pkv, wl)
+        line["mixed_batch"] = {
+            "workload": "4 prefill chunks (2048 cached + 512) + 28 decode rows (ctx U[512,4096]), "
+                        "8q/2kv heads, D256, bf16, softcap 50",
+            "mixed_call_ms": round(mx_ms, 5), "one_prefill_launch_ms": round(one_ms, 5)}
         for maker in (wl.sliding_window_decode, wl.long_context_splitk):
             c = maker()
             b = DecodeBench(c, 0, torch, pkv)

@@ -59,6 +59,8 @@ SIGNATURES = {
                                                _I, _I, _I]),
     "pkv_decode_graph_launch": (ctypes.c_int, [_P, _P]),
     "pkv_decode_graph_destroy": (None, [_P]),
+    "paged_attn_mixed": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I,
+                                        _I, _I, _I, _I, _F, _F, _I, _P, _Z, _I, _P]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
 
@@ -487,3 +489,36 @@ __all__ = [
     "paged_attn_decode", "paged_attn_decode_splitk", "paged_attn_prefill", "decode_workspace",
     "from_bits", "to_bits",
 ]
+
+
+def paged_attn_mixed(out, q, cu_q_lens, num_prefill_tokens, max_q_len, k_pool, v_pool,
+                     block_tables, context_lens, max_context_len, scale, softcap=0.0, window=0,
+                     lse=None, workspace=None, stream=None) -> None:
+    """A mixed batch: the ``len(cu_q_lens) - 1`` first sequences are prefill
+    chunks (rows ``0 .. num_prefill_tokens - 1``), the others decode rows (one
+    row each, after the chunks' rows)."""
+    nb, hkv, d = _pool_dims(k_pool, v_pool)
+    T, hq, dq = q.shape
+    B = context_lens.numel()
+    P = cu_q_lens.numel() - 1
+    if dq != d or hq % hkv or not 0 <= P <= B or T != num_prefill_tokens + B - P:
+        raise ValueError("q rows must be the chunks' rows followed by one row per decode sequence")
+    if tuple(out.shape) != tuple(q.shape) or out.dtype != q.dtype or q.dtype != k_pool.dtype:
+        raise ValueError("out must match q, and q's dtype the pools'")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables [B, MB] and context_lens [B] disagree")
+    G = hq // hkv
+    ws = workspace
+    if ws is None and B > P:
+        ws = decode_workspace(paged_attn_decode_workspace_size(B - P, hkv, G, d, max_context_len, 0),
+                              q.device, stream)
+    lib = load_library()
+    rc = lib.paged_attn_mixed(_ptr(out), _ptr(lse), _ptr(q),
+                              _i32(cu_q_lens, "cu_q_lens") if P > 0 else None, P,
+                              int(num_prefill_tokens), int(max_q_len), _ptr(k_pool), _ptr(v_pool),
+                              nb, _i32(block_tables, "block_tables"), block_tables.shape[1],
+                              _i32(context_lens, "context_lens"), int(max_context_len), B, hkv, G,
+                              d, BLOCK_SIZE, float(scale), float(softcap), int(window), _ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size(), _dtype_code(q),
+                              _stream(stream))
+    _check("paged_attn_mixed", rc)

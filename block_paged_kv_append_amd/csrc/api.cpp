@@ -436,4 +436,43 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q
                   fn);
 }
 
+int paged_attn_mixed(void* out, float* lse, const void* q, const int32_t* cu_q_lens,
+                     int32_t num_prefill_seqs, int32_t num_prefill_tokens, int32_t max_q_len,
+                     const void* k_pool, const void* v_pool, int32_t num_blocks,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                     int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                     int32_t block_size, float scale, float softcap, int32_t window,
+                     void* workspace, size_t workspace_bytes, int32_t dtype,
+                     struct ihipStream_t* stream) {
+  const char* fn = "paged_attn_mixed";
+  if (num_prefill_seqs < 0 || num_prefill_seqs > num_seqs || num_prefill_tokens < 0 ||
+      (num_prefill_seqs == 0) != (num_prefill_tokens == 0))
+    return fail(PKV_EINVAL, "%s: %d prefill sequences / %d prefill rows of %d sequences", fn,
+                num_prefill_seqs, num_prefill_tokens, num_seqs);
+  const int es = elem_bytes(dtype);
+  if (es == 0) return fail(PKV_EUNSUPPORTED, "%s: dtype %d", fn, dtype);
+  const int32_t P = num_prefill_seqs, Bd = num_seqs - num_prefill_seqs;
+  const size_t row = (size_t)num_kv_heads * gqa_group * head_dim * es;  // one q / out row
+  int rc = PKV_OK;
+  if (P > 0) {
+    rc = paged_attn_prefill(out, lse, q, cu_q_lens, num_prefill_tokens, max_q_len, k_pool, v_pool,
+                            num_blocks, block_tables, max_blocks_per_seq, context_lens,
+                            max_context_len, P, num_kv_heads, gqa_group, head_dim, block_size,
+                            scale, softcap, window, dtype, stream);
+    if (rc != PKV_OK) return rc;
+  }
+  if (Bd > 0) {
+    char* o = static_cast<char*>(out) + (size_t)num_prefill_tokens * row;
+    const char* qd = static_cast<const char*>(q) + (size_t)num_prefill_tokens * row;
+    float* ld = lse ? lse + (size_t)num_prefill_tokens * num_kv_heads * gqa_group : nullptr;
+    rc = decode_impl(fn, o, ld, qd, DecodeExtras{}, k_pool, v_pool, num_blocks,
+                     block_tables + (size_t)P * max_blocks_per_seq, max_blocks_per_seq,
+                     context_lens + P, max_context_len, Bd, num_kv_heads, gqa_group, head_dim,
+                     block_size, scale, softcap, window, 0, workspace, workspace_bytes, dtype,
+                     reinterpret_cast<hipStream_t>(stream));
+  }
+  return rc;
+}
+
 }  // extern "C"

@@ -349,6 +349,38 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q
                        int32_t gqa_group, int32_t head_dim, int32_t block_size, float scale,
                        float softcap, int32_t window, int32_t dtype, struct ihipStream_t* stream);
 
+/*
+ * paged_attn_mixed -- one call for a batch that mixes prefill chunks with
+ * decode rows: the engine interleaves chunked prefill with the decode of the
+ * other active requests, tick by tick (page "Inference Server -- Architecture
+ * Map", section "How a single request flows through the system").
+ *
+ * Sequences [0, num_prefill_seqs) are chunks: their rows are
+ * cu_q_lens[b] .. cu_q_lens[b+1]-1 of q / out (cu_q_lens has
+ * num_prefill_seqs + 1 entries, the last = num_prefill_tokens), as in
+ * paged_attn_prefill.  Sequences [num_prefill_seqs, num_seqs) are decode
+ * rows: one query each, rows num_prefill_tokens + (b - num_prefill_seqs).
+ * block_tables / context_lens cover all num_seqs sequences in that order.
+ * The result is that of paged_attn_prefill over the whole batch (a decode row
+ * is a one-row chunk), but the chunks run through the prefill kernel and the
+ * decode rows through the balanced decode split, which spreads a long row
+ * over every compute unit (two launches on `stream`).
+ *   out, q, lse   [num_prefill_tokens + num_seqs - num_prefill_seqs, Hq, D]
+ *   workspace     >= paged_attn_decode_workspace_size(num_seqs -
+ *                 num_prefill_seqs, ..., 0) bytes when there are decode rows
+ * Errors as paged_attn_prefill and paged_attn_decode; PKV_EINVAL for counts
+ * that do not fit.
+ */
+int paged_attn_mixed(void* out, float* lse, const void* q, const int32_t* cu_q_lens,
+                     int32_t num_prefill_seqs, int32_t num_prefill_tokens, int32_t max_q_len,
+                     const void* k_pool, const void* v_pool, int32_t num_blocks,
+                     const int32_t* block_tables, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                     int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
+                     int32_t block_size, float scale, float softcap, int32_t window,
+                     void* workspace, size_t workspace_bytes, int32_t dtype,
+                     struct ihipStream_t* stream);
+
 /* Message describing the calling thread's last failed call ("" if none). */
 const char* pkv_last_error(void);
 

@@ -301,3 +301,29 @@ def test_mixed_batch_decode_rows_and_chunks(D, cap, W):
                                   case.context_lens, case.scale, case.softcap, case.window, "bf16")
     check_close(out, ref, "bf16", "mixed batch")
     check_lse(lse, ref_lse, "mixed batch")
+
+
+@pytest.mark.parametrize("D,cap,W", [(128, 0.0, 0), (256, 50.0, 0), (256, 0.0, 300), (64, 0.0, 0)])
+def test_mixed_call_chunks_then_decode_rows(D, cap, W):
+    """paged_attn_mixed: prefill chunks first, decode rows after them; the
+    result equals the oracle's prefill over the whole batch."""
+    cached = [700, 64, 33, 100, 2000, 31, 1500, 0]
+    chunk = [300, 64, 17, 1, 1, 1, 1, 1]
+    P = 3
+    case = wl.make_prefill_case(490 + D + W, cached, chunk, 8, 2, D, "bf16", softcap=cap, window=W)
+    banner("mixed call", D, cap, W)
+    kp, vp = run_append(case)
+    q = dev(case.q, "bf16")
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    cu = case.cu_q_lens[:P + 1]
+    pkv.paged_attn_mixed(out, q, i32(cu), int(cu[-1]), int(max(chunk[:P])), kp, vp,
+                         i32(case.block_tables), i32(case.context_lens), case.max_context_len,
+                         case.scale, case.softcap, case.window, lse=lse)
+    torch.cuda.synchronize()
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           "bf16")
+    ref, ref_lse = oracle.prefill(case.q, case.cu_q_lens, kr, vr, case.block_tables,
+                                  case.context_lens, case.scale, case.softcap, case.window, "bf16")
+    check_close(out.float().cpu().numpy().astype(np.float64), ref, "bf16", "mixed call")
+    check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, "mixed call")
