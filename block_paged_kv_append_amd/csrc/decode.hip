@@ -734,7 +734,13 @@ __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const 
 }
 
 // LDS bytes of the ring each wave of the LDS form streams its blocks through
-constexpr int kRingBytesPerWave = 32768;
+// (two blocks of 16 KiB at head_dim 256), and workgroups per CU: at head_dim
+// <= 128 two workgroups share a CU (16 KiB rings, 2 or 4 blocks in flight per
+// wave), so one's start-up overlaps the other's streaming.
+template <int D>
+constexpr int kRingBytesPerWave = D >= 256 ? 32768 : 16384;
+template <int D>
+constexpr int kRingWgsPerCu = D >= 256 ? 1 : 2;
 
 // One piece, bf16, blocks streamed through LDS.  As run_piece_bf16 (each wave
 // walks its own blocks, O^T on the matrix cores, waves combined at the end),
@@ -750,7 +756,7 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   constexpr int XT = D / 16;                        // output tiles
   constexpr int kTileBytes = D * kBlock * 2;        // one block's K (or V)
   constexpr int kRuns = 2 * kTileBytes / 1024;      // 1 KiB copies per block
-  constexpr int NS = kRingBytesPerWave / (2 * kTileBytes);
+  constexpr int NS = kRingBytesPerWave<D> / (2 * kTileBytes);
   static_assert(NS >= 2, "at least two blocks per wave in flight");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -788,7 +794,7 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   auto tbl_at = [&](int idx) { return EVICT ? bt[sk.blk(sp, j0 + wave + kWaves * idx)] : bt[kWaves * idx]; };
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
-  char* ring = reinterpret_cast<char*>(lds) + wave * kRingBytesPerWave;
+  char* ring = reinterpret_cast<char*>(lds) + wave * kRingBytesPerWave<D>;
   NewToken<2, D> nt;
   if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
   // this wave's table entries, 64 at a time (lane l: block tbase + l)
@@ -951,7 +957,7 @@ __device__ void finish_split(const DecodeArgs& a, int b, int g, SlotList slots, 
 }
 
 template <bool BF16, int D, bool FIXED, bool FUSE, bool EVICT>
-__global__ __launch_bounds__(kThreads, (BF16 && !kRingForm<D>) ? 2 : 1) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<D> : 2) void decode_kernel(DecodeArgs a) {
   extern __shared__ float lds[];
   auto run_one = [&](const LogitXform& xf, const Piece& pc) {
     if constexpr (BF16) {
@@ -1121,13 +1127,14 @@ hipError_t launch_d(DecodeArgs a, hipStream_t stream) {
   if (a.part_blocks == 0) {
     long long n = (a.units_bound + PKV_DECODE_MIN_BLOCKS_PER_WG - 1) / PKV_DECODE_MIN_BLOCKS_PER_WG;
     const long long cap =
-        (long long)a.cu_count * (BF16 && !kRingForm<D> ? PKV_DECODE_BF16_WGS_PER_CU : PKV_DECODE_WGS_PER_CU);
+        (long long)a.cu_count * (!BF16 ? PKV_DECODE_WGS_PER_CU
+                                       : kRingForm<D> ? kRingWgsPerCu<D> : PKV_DECODE_BF16_WGS_PER_CU);
     n = min(n, min(cap, (long long)kMaxWorkers));
     a.num_workers = (int32_t)max(n, 1LL);
   }
   size_t lds = (size_t)kWaves * a.gqa_group * (D + 2) * sizeof(float);  // the waves' combine
   lds = std::max(lds, (size_t)(4 * kThreads + 2 * 16) * sizeof(float));  // a merge
-  if (BF16 && kRingForm<D>) lds = std::max(lds, (size_t)kWaves * kRingBytesPerWave);
+  if (BF16 && kRingForm<D>) lds = std::max(lds, (size_t)kWaves * kRingBytesPerWave<D>);
   if (a.part_blocks > 0)
     return a.k_new ? launch_k(decode_kernel<BF16, D, true, true, false>, a, lds, stream)
                    : launch_k(decode_kernel<BF16, D, true, false, false>, a, lds, stream);
