@@ -215,82 +215,91 @@ __device__ __forceinline__ void finalize_vec(const DecodeArgs& a, int b, int h_g
     a.lse[(size_t)b * Hq + h_global] = L > 0.f ? (M + fast_log2(L)) * kLn2 : kNegInf;
 }
 
-// Merge the partials listed by `slots` for query head h of segment (b, g)
-// and write its output row.  Thread (group, lane) takes the slots k = group,
-// group + kGroups, ... for dims 4 lane .. 4 lane + 3; it issues the loads of
-// up to kPer slots at once, then folds them into a running (max, sum,
-// output); the groups are folded through LDS at the end.
+// Merge the partials listed by `slots` for every query head of segment (b, g)
+// and write the segment's output rows.  The G heads x D/4 float4 columns are
+// spread over the threads; when they number fewer than the threads, the
+// threads form `groups` copies of them and copy r takes the slots r,
+// r + groups, ...  A thread issues the loads of up to kPer slots at once,
+// then folds them into a running (max, sum, output); the copies are folded
+// through LDS at the end.  All heads are merged in one pass, so the loads of
+// the G rows are in flight together.
 template <bool BF16, int D, typename SlotList, bool V = false>
-__device__ void merge_row(const DecodeArgs& a, int b, int g, int h, SlotList slots, float* lds) {
-  constexpr int kLanes = D / 4;                 // float4 columns per row
-  constexpr int kGroups = kThreads / kLanes;    // slot groups (16, 8 or 4)
-  constexpr int kPer = 8;                       // slots in flight per thread
+__device__ void merge_segment(const DecodeArgs& a, int b, int g, SlotList slots, float* lds) {
+  constexpr int kLanes = D / 4;  // float4 columns per row
+  constexpr int kPer = 8;        // slots in flight per thread
   const int G = a.gqa_group;
-  const int col = threadIdx.x % kLanes, grp = threadIdx.x / kLanes;
-  float M = kNegInf, L = 0.f;
-  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  const int R = G * kLanes;      // (head, column) pairs
+  const int groups = R >= kThreads ? 1 : kThreads / R;
   const int cnt = slots.count();
-  for (int k0 = grp; k0 < cnt; k0 += kGroups * kPer) {
-    float mk[kPer], lk[kPer];
-    f32x4 ov[kPer];
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) {
-      const int k = k0 + q * kGroups;
-      int sl = 0;
-      const bool valid = k < cnt && slots.slot(k, sl);
-      lk[q] = 0.f;
-      mk[q] = kNegInf;
-      ov[q] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (valid) {
-        mk[q] = load_dev(a.part_ml + ((size_t)sl * G + h) * 2);
-        lk[q] = load_dev(a.part_ml + ((size_t)sl * G + h) * 2 + 1);
-        const float* po = a.part_o + ((size_t)sl * G + h) * D + 4 * col;
-        ov[q] = f32x4{load_dev(po), load_dev(po + 1), load_dev(po + 2), load_dev(po + 3)};
-      }
-    }
-    float Mn = M;
-#pragma unroll
-    for (int q = 0; q < kPer; ++q) Mn = lk[q] > 0.f ? fmaxf(Mn, mk[q]) : Mn;
-    if (Mn != kNegInf) {
-      const float sa = fast_exp2(M - Mn);  // 0 when M = -inf
-      O = O * sa;
-      L = L * sa;
+  for (int e0 = 0; e0 < R; e0 += kThreads) {
+    const int e = groups > 1 ? (int)threadIdx.x % R : e0 + (int)threadIdx.x;
+    const int grp = groups > 1 ? (int)threadIdx.x / R : 0;
+    const bool active = e < R && grp < groups;
+    const int h = e / kLanes, col = e % kLanes;
+    float M = kNegInf, L = 0.f;
+    f32x4 O = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = grp; active && k0 < cnt; k0 += groups * kPer) {
+      float mk[kPer], lk[kPer];
+      f32x4 ov[kPer];
 #pragma unroll
       for (int q = 0; q < kPer; ++q) {
-        const float sb = lk[q] > 0.f ? fast_exp2(mk[q] - Mn) : 0.f;
-        O += ov[q] * sb;
-        L += lk[q] * sb;
-      }
-      M = Mn;
-    }
-  }
-  if constexpr (kGroups > 1) {
-    f32x4* lo = reinterpret_cast<f32x4*>(lds);          // [kGroups][kLanes]
-    float* lml = lds + 4 * kGroups * kLanes;             // [kGroups][2]
-    lo[grp * kLanes + col] = O;
-    if (col == 0) {
-      lml[2 * grp] = M;
-      lml[2 * grp + 1] = L;
-    }
-    __syncthreads();
-    if (grp == 0) {
-      float Mt = kNegInf;
-#pragma unroll
-      for (int q = 0; q < kGroups; ++q) Mt = fmaxf(Mt, lml[2 * q]);
-      O = f32x4{0.f, 0.f, 0.f, 0.f};
-      L = 0.f;
-      if (Mt != kNegInf) {
-#pragma unroll
-        for (int q = 0; q < kGroups; ++q) {
-          const float sc = fast_exp2(lml[2 * q] - Mt);
-          O += lo[q * kLanes + col] * sc;
-          L += lml[2 * q + 1] * sc;
+        const int k = k0 + q * groups;
+        int sl = 0;
+        const bool valid = k < cnt && slots.slot(k, sl);
+        lk[q] = 0.f;
+        mk[q] = kNegInf;
+        ov[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (valid) {
+          mk[q] = load_dev(a.part_ml + ((size_t)sl * G + h) * 2);
+          lk[q] = load_dev(a.part_ml + ((size_t)sl * G + h) * 2 + 1);
+          const float* po = a.part_o + ((size_t)sl * G + h) * D + 4 * col;
+          ov[q] = f32x4{load_dev(po), load_dev(po + 1), load_dev(po + 2), load_dev(po + 3)};
         }
       }
-      M = Mt;
+      float Mn = M;
+#pragma unroll
+      for (int q = 0; q < kPer; ++q) Mn = lk[q] > 0.f ? fmaxf(Mn, mk[q]) : Mn;
+      if (Mn != kNegInf) {
+        const float sa = fast_exp2(M - Mn);  // 0 when M = -inf
+        O = O * sa;
+        L = L * sa;
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+          const float sb = lk[q] > 0.f ? fast_exp2(mk[q] - Mn) : 0.f;
+          O += ov[q] * sb;
+          L += lk[q] * sb;
+        }
+        M = Mn;
+      }
     }
+    if (groups > 1) {
+      f32x4* lo = reinterpret_cast<f32x4*>(lds);  // [groups][R]
+      float* lml = lds + 4 * groups * R;           // [groups][G][2]
+      if (active) {
+        lo[grp * R + e] = O;
+        if (col == 0) {
+          lml[2 * (grp * G + h)] = M;
+          lml[2 * (grp * G + h) + 1] = L;
+        }
+      }
+      __syncthreads();
+      if (active && grp == 0) {
+        float Mt = kNegInf;
+        for (int q = 0; q < groups; ++q) Mt = fmaxf(Mt, lml[2 * (q * G + h)]);
+        O = f32x4{0.f, 0.f, 0.f, 0.f};
+        L = 0.f;
+        if (Mt != kNegInf) {
+          for (int q = 0; q < groups; ++q) {
+            const float sc = fast_exp2(lml[2 * (q * G + h)] - Mt);
+            O += lo[q * R + e] * sc;
+            L += lml[2 * (q * G + h) + 1] * sc;
+          }
+        }
+        M = Mt;
+      }
+    }
+    if (active && grp == 0) finalize_vec<BF16, D>(a, b, g * G + h, 4 * col, O, L, M);
   }
-  if (grp == 0) finalize_vec<BF16, D>(a, b, g * G + h, 4 * col, O, L, M);
 }
 
 struct SplitSlots {  // fixed partitions p_lo .. p_hi of one segment
@@ -951,7 +960,7 @@ __device__ void finish_split(const DecodeArgs& a, int b, int g, SlotList slots, 
   const bool last = flag[0] != 0;
   __syncthreads();  // LDS is reused below
   if (!last) return;
-  for (int h = 0; h < a.gqa_group; ++h) merge_row<BF16, D, SlotList, V>(a, b, g, h, slots, lds);
+  merge_segment<BF16, D, SlotList, V>(a, b, g, slots, lds);
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
 }
