@@ -42,8 +42,7 @@
 #include "attn_tile.hpp"
 #include "launch.hpp"
 
-// bf16: blocks streamed through per-wave LDS rings at every head_dim (32 KiB
-// per wave: 2, 4 or 8 blocks in flight at head_dim 256, 128, 64).  The
+// bf16: blocks streamed through per-wave LDS rings at every head_dim.  The
 // register form (blocks loaded into registers, two workgroups per CU) is kept
 // switched off: runs of its head_dim 64 / 128 instantiations gave wrong
 // results and memory faults whose cause was not found.
@@ -311,16 +310,20 @@ struct SplitSlots {  // fixed partitions p_lo .. p_hi of one segment
   }
 };
 
-// Workgroups whose ranges meet [S, E).  With W > N every range holds at
-// least one unit, so they are w_first .. w_last.  With W <= N a range holds
-// one unit or none, and the workgroups with an empty range (which store
-// nothing and never count in) lie between those; the pieces are then the
-// owners of units S .. E - 1, one each.
+// Workgroups whose ranges meet the real units [S, E) of a segment, in the
+// split's coordinates (real units plus kPieceCost<D> cost units in front of
+// every segment, see decode_kernel); Sv = S - kPieceCost<D> is where the
+// segment's cost units start.  With W > N every range holds at least one
+// unit, so they are w_first .. w_last.  With W <= N a range holds one unit or
+// none, and the workgroups with an empty range (which store nothing and never
+// count in) lie between those; the pieces are then the owners of units S ..
+// E - 1, one each.  A workgroup whose range starts at or after Sv met the
+// segment first (slot 2 w), otherwise second (slot 2 w + 1).
 struct BalancedSlots {
-  long long W, S, E;
+  long long W, S, E, Sv;
   int N, w_first, w_last;
-  __device__ BalancedSlots(long long W_, long long S_, long long E_, int N_)
-      : W(W_), S(S_), E(E_), N(N_) {
+  __device__ BalancedSlots(long long W_, long long S_, long long E_, long long Sv_, int N_)
+      : W(W_), S(S_), E(E_), Sv(Sv_), N(N_) {
     w_first = (int)(((S + 1) * N - 1) / W);
     w_last = (int)((E * N - 1) / W);
   }
@@ -328,7 +331,7 @@ struct BalancedSlots {
   __device__ bool slot(int k, int& s) const {
     const int w = W <= N ? (int)(((S + k + 1) * N - 1) / W) : w_first + k;
     const long long a0 = (long long)w * W / N;
-    s = a0 < S ? 2 * w + 1 : 2 * w;
+    s = a0 < Sv ? 2 * w + 1 : 2 * w;
     return true;
   }
 };
@@ -751,6 +754,14 @@ constexpr int kRingBytesPerWave = D >= 256 ? 32768 : 16384;
 template <int D>
 constexpr int kRingWgsPerCu = D >= 256 ? 1 : 2;
 
+// The balanced split's price of one piece (its start, partial store and
+// merge), in cache blocks of one kv head: PKV_DECODE_PIECE_COST_BYTES of K/V.
+#ifndef PKV_DECODE_PIECE_COST_BYTES
+#define PKV_DECODE_PIECE_COST_BYTES (192 * 1024)
+#endif
+template <int D>
+constexpr int kPieceCost = PKV_DECODE_PIECE_COST_BYTES / (2 * kBlock * D * 2);
+
 // One piece, bf16, blocks streamed through LDS.  As run_piece_bf16 (each wave
 // walks its own blocks, O^T on the matrix cores, waves combined at the end),
 // but K and V reach LDS by direct buffer-to-LDS copies into a ring private to
@@ -1023,12 +1034,18 @@ __global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<
         write_empty<BF16, D, EVICT>(a, b, 0, Hkv * G);
     }
 
-    // total units W (every wave computes the same value)
+    // The split runs over W = sum of (kPieceCost<D> + nb) x Hkv units: every
+    // segment's nb real units preceded by kPieceCost<D> units that stand for
+    // the fixed cost of a piece (its start, partial store and merge), so that
+    // a workgroup whose range crosses into another segment takes fewer real
+    // units.  Every wave computes the same W.
+    constexpr int C = kPieceCost<D>;
+    auto seg_units = [&](int nb) -> long long { return nb > 0 ? (long long)(nb + C) : 0; };
     long long W = 0;
     for (int base = 0; base < B; base += kWave) {
       const int b = base + lane;
       const int nb = b < B ? span(a.context_lens[b]).nb : 0;
-      W += wave_sum_i64(nb);
+      W += wave_sum_i64(seg_units(nb));
     }
     W *= Hkv;
     const long long a0 = (long long)w * W / N, a1 = (long long)(w + 1) * W / N;
@@ -1039,9 +1056,7 @@ __global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<
     int b0 = 0;
     for (int base = 0; base < B; base += kWave) {
       const int b = base + lane;
-      const long long nbh =
-          b < B ? (long long)span(a.context_lens[b]).nb * Hkv
-                : 0;
+      const long long nbh = b < B ? seg_units(span(a.context_lens[b]).nb) * Hkv : 0;
       const long long incl = wave_incl_scan_i64(nbh, lane);
       const unsigned long long hit = __ballot(run + incl > a0);
       if (hit) {
@@ -1056,22 +1071,24 @@ __global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<
     Piece pc;
     pc.b = b0;
     pc.sp = span(a.context_lens[b0]);
-    pc.g = (int)((a0 - seg_base) / pc.sp.nb);
-    pc.S = seg_base + (long long)pc.g * pc.sp.nb;
-    long long pos = a0;
+    pc.g = (int)((a0 - seg_base) / (pc.sp.nb + C));
+    long long Sv = seg_base + (long long)pc.g * (pc.sp.nb + C);  // segment start (cost units)
     bool first = true;
-    while (pos < a1) {
-      const long long E = pc.S + pc.sp.nb;
-      pc.j0 = (int)(pos - pc.S);
-      pc.j1 = (int)(min(a1, E) - pc.S);
-      pc.slot = first ? 2 * w : 2 * w + 1;
-      run_one(xf, pc);
-      if (!(pc.j0 == 0 && pc.j1 == pc.sp.nb))
-        finish_split<BF16, D, EVICT>(a, pc.b, pc.g, BalancedSlots{W, pc.S, E, N}, lds);
+    while (true) {
+      const long long S = Sv + C, E = S + pc.sp.nb;  // the segment's real units
+      const long long lo = max(a0, S), hi = min(a1, E);
+      if (lo < hi) {
+        pc.S = S;
+        pc.j0 = (int)(lo - S);
+        pc.j1 = (int)(hi - S);
+        pc.slot = first ? 2 * w : 2 * w + 1;
+        run_one(xf, pc);
+        if (!(pc.j0 == 0 && pc.j1 == pc.sp.nb))
+          finish_split<BF16, D, EVICT>(a, pc.b, pc.g, BalancedSlots{W, S, E, Sv, N}, lds);
+      }
       first = false;
-      pos = E;
-      pc.S = E;
-      if (pos >= a1) break;
+      Sv = E;
+      if (Sv >= a1) break;
       if (++pc.g == Hkv) {
         pc.g = 0;
         do {
