@@ -815,11 +815,13 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
   char* ring = reinterpret_cast<char*>(lds) + wave * kRingBytesPerWave<D>;
-  NewToken<2, D> nt;
-  if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
-  // this wave's table entries, 64 at a time (lane l: block tbase + l)
+  // this wave's table entries, 64 at a time (lane l: block tbase + l); loaded
+  // before the fused append's set-up, whose own table read and branch would
+  // otherwise hold this load back
   int tbase = 0;
   int tbl = lane < nw ? tbl_at(lane) : 0;
+  NewToken<2, D> nt;
+  if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
   uint32_t okbits = 0;  // bit (block % NS): that slot's block was readable
 
   // copy this wave's block i (past the end: an empty range, zeros) into its slot
@@ -1028,10 +1030,33 @@ __global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<
     const int lane = threadIdx.x & 63;
     const int B = a.num_seqs;
 
+    // Context lengths of sequences 64 r + lane, r < kLenRegs, held in
+    // registers: one load for the whole set-up below (the work total, the
+    // scan for this workgroup's first segment, its span and the empty
+    // sequences), so that the chain before the first K/V copies is the
+    // lengths, then the block table.  Longer batches read the rest as needed.
+    constexpr int kLenRegs = 4;
+    int Lr[kLenRegs];
+#pragma unroll
+    for (int r = 0; r < kLenRegs; ++r) {
+      const int b = r * kWave + lane;
+      Lr[r] = b < B ? a.context_lens[b] : 0;
+    }
+    auto len_at = [&](int r) -> int {  // length of sequence 64 r + lane (0 past B)
+      int L = 0;
+#pragma unroll
+      for (int q = 0; q < kLenRegs; ++q) L = q == r ? Lr[q] : L;
+      if (r >= kLenRegs) {
+        const int b = r * kWave + lane;
+        L = b < B ? a.context_lens[b] : 0;
+      }
+      return L;
+    };
+
     // sequences with no visible token
     for (int b = w; b < B; b += N) {
-      if (span(a.context_lens[b]).nb == 0)
-        write_empty<BF16, D, EVICT>(a, b, 0, Hkv * G);
+      const int L = __builtin_amdgcn_readlane(len_at(b / kWave), b % kWave);
+      if (span(L).nb == 0) write_empty<BF16, D, EVICT>(a, b, 0, Hkv * G);
     }
 
     // The split runs over W = sum of (kPieceCost<D> + nb) x Hkv units: every
@@ -1042,26 +1067,23 @@ __global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<
     constexpr int C = kPieceCost<D>;
     auto seg_units = [&](int nb) -> long long { return nb > 0 ? (long long)(nb + C) : 0; };
     long long W = 0;
-    for (int base = 0; base < B; base += kWave) {
-      const int b = base + lane;
-      const int nb = b < B ? span(a.context_lens[b]).nb : 0;
-      W += wave_sum_i64(seg_units(nb));
-    }
+    for (int r = 0; r * kWave < B; ++r) W += wave_sum_i64(seg_units(span(len_at(r)).nb));
     W *= Hkv;
     const long long a0 = (long long)w * W / N, a1 = (long long)(w + 1) * W / N;
     if (a0 >= a1) return;
 
     // segment holding unit a0: first sequence whose inclusive prefix exceeds a0
     long long run = 0, seg_base = 0;
-    int b0 = 0;
-    for (int base = 0; base < B; base += kWave) {
-      const int b = base + lane;
-      const long long nbh = b < B ? seg_units(span(a.context_lens[b]).nb) * Hkv : 0;
+    int b0 = 0, L0 = 0;
+    for (int r = 0; r * kWave < B; ++r) {
+      const int Lb = len_at(r);
+      const long long nbh = seg_units(span(Lb).nb) * Hkv;
       const long long incl = wave_incl_scan_i64(nbh, lane);
       const unsigned long long hit = __ballot(run + incl > a0);
       if (hit) {
         const int l0 = __ffsll(hit) - 1;
-        b0 = base + l0;
+        b0 = r * kWave + l0;
+        L0 = __builtin_amdgcn_readlane(Lb, l0);
         seg_base = run + __shfl(incl - nbh, l0);
         break;
       }
@@ -1070,7 +1092,7 @@ __global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<
 
     Piece pc;
     pc.b = b0;
-    pc.sp = span(a.context_lens[b0]);
+    pc.sp = span(L0);
     pc.g = (int)((a0 - seg_base) / (pc.sp.nb + C));
     long long Sv = seg_base + (long long)pc.g * (pc.sp.nb + C);  // segment start (cost units)
     bool first = true;

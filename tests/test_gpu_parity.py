@@ -165,6 +165,23 @@ def test_decode_more_workgroups_than_blocks():
     assert int(ws[:4 * 8].view(torch.int32).abs().sum()) == 0  # counters back at zero
 
 
+@pytest.mark.gpu
+@pytest.mark.parametrize("B", [65, 300])
+def test_decode_large_batch(B):
+    """Batches past one wave of lengths (65) and past the lengths the balanced
+    split holds in registers (300: sequences 256 and up are read as needed),
+    with empty sequences among them."""
+    rng = np.random.default_rng(360 + B)
+    lens = rng.integers(0, 200, size=B)
+    lens[rng.choice(B, size=5, replace=False)] = 0
+    case = wl.make_decode_case(361 + B, [int(x) for x in lens], 8, 2, 64, "bf16", softcap=30.0)
+    banner("decode large batch", B)
+    out, lse = run_decode(case)
+    ref, ref_lse = oracle_decode(case)
+    check_close(out, ref, "bf16", f"B={B}")
+    check_lse(lse, ref_lse, f"B={B}")
+
+
 # ---------------------------------------------------------------------------
 # the named workloads at full size
 # ---------------------------------------------------------------------------
