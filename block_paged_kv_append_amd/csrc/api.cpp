@@ -178,6 +178,10 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const Deco
   base += align256(slots * gqa_group * head_dim * sizeof(float));
   a.part_ml = reinterpret_cast<float*>(base);
 
+  int cus = 0;
+  rc = cu_count(&cus);
+  if (rc != PKV_OK) return rc;
+  a.cu_count = cus;
   if (partition_size > 0) {
     const int np = (max_context_len + partition_size - 1) / partition_size;
     const long long grid = (long long)num_seqs * num_kv_heads * (np > 0 ? np : 1);
@@ -186,10 +190,6 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const Deco
     a.num_partitions = np > 0 ? np : 1;
     a.num_workers = (int32_t)grid;
   } else {
-    int cus = 0;
-    rc = cu_count(&cus);
-    if (rc != PKV_OK) return rc;
-    a.cu_count = cus;
     a.units_bound =
         (long long)num_seqs * num_kv_heads * max_units_per_seq(max_context_len, window, x.sink);
     a.part_blocks = 0;

@@ -339,6 +339,28 @@ struct BalancedSlots {
 // The four waves' (max, sum, output) of one piece, in LDS as lo[wave][head][D]
 // and lml[wave][head][2]: merged, then written as the output (whole segment)
 // or as the piece's partial.
+// Pieces of the persistent split-K decode within one segment's items
+// [S, E) (of I items split over N workgroups): the workgroups whose item
+// ranges meet [S, E), each storing one partial at the slot of its first
+// partition in the segment (base + its first item - S).  With I <= N a range
+// holds one item or none, and the pieces are the owners of items S .. E - 1.
+struct RunSlots {
+  long long I, S, E;
+  int N, base, w_first, w_last;
+  __device__ RunSlots(long long I_, long long S_, long long E_, int N_, int base_)
+      : I(I_), S(S_), E(E_), N(N_), base(base_) {
+    w_first = (int)(((S + 1) * N - 1) / I);
+    w_last = (int)((E * N - 1) / I);
+  }
+  __device__ int count() const { return I <= N ? (int)(E - S) : w_last - w_first + 1; }
+  __device__ bool slot(int k, int& s) const {
+    const int w = I <= N ? (int)(((S + k + 1) * N - 1) / I) : w_first + k;
+    const long long first = max(S, (long long)w * I / N);
+    s = base + (int)(first - S);
+    return true;
+  }
+};
+
 template <bool BF16, int D, bool V = false>
 __device__ void combine_waves(const DecodeArgs& a, const Piece& pc, const float* lo, const float* lml) {
   const int G = a.gqa_group;
@@ -756,6 +778,10 @@ constexpr int kRingWgsPerCu = D >= 256 ? 1 : 2;
 
 // The balanced split's price of one piece (its start, partial store and
 // merge), in cache blocks of one kv head: PKV_DECODE_PIECE_COST_BYTES of K/V.
+// split-K decode through the persistent kernel (0: one workgroup per partition)
+#ifndef PKV_DECODE_FIXED_STREAM
+#define PKV_DECODE_FIXED_STREAM 1
+#endif
 #ifndef PKV_DECODE_PIECE_COST_BYTES
 #define PKV_DECODE_PIECE_COST_BYTES (192 * 1024)
 #endif
@@ -945,6 +971,269 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   __syncthreads();  // LDS is reused by the next piece
 }
 
+// ---------------------------------------------------------------------------
+// Split-K decode (fixed partitions), persistent form.  One workgroup per CU
+// takes a contiguous run of the (segment, partition) items -- the visible
+// partitions of every segment, segment after segment -- and streams their
+// blocks through per-wave LDS rings that carry over from one partition to the
+// next: while a partition is combined and its partial stored, the next one's
+// first blocks are already being copied.  A workgroup counts its partitions
+// of a segment in with one atomic add when it leaves the segment; the one
+// that completes the count merges the segment.  The result is the same as
+// one workgroup per partition (same partials, same merge), without a round of
+// workgroup start-ups per partition.
+// ---------------------------------------------------------------------------
+constexpr int kStreamRingBytes = 32768;  // per wave
+constexpr int kDummyBytes = 1024;        // takes the empty prologue copies
+template <int D>
+__host__ __device__ constexpr int combine_bytes(int G) {
+  return kWaves * G * (D + 2) * 4 > (4 * kThreads + 2 * 16) * 4 ? kWaves * G * (D + 2) * 4
+                                                                  : (4 * kThreads + 2 * 16) * 4;
+}
+template <int D>
+__host__ __device__ constexpr int fixed_stream_lds(int G) {
+  return kWaves * kStreamRingBytes + combine_bytes<D>(G) + kDummyBytes;
+}
+constexpr int kLdsPerCu = 163840;
+
+// A wave's LDS ring carried from one partition to the next.  Block k of the
+// current partition sits at stream position pos + k, ring slot (pos + k) % NS.
+// When the next partition gives this wave at least NS blocks, the current one
+// loads its table slice and query fragments when it starts and issues its
+// first NS blocks in its own last NS steps.
+template <int D>
+struct RingStream {
+  int pos = 0;
+  uint32_t okbits = 0;  // bit (position % NS): that slot's block was readable
+  bool pre = false;     // the current partition's first NS blocks are issued
+  bool qpre = false;    // its query fragments are in qn
+  int tbl = 0;          // its table slice (lane l: block l of this wave), if pre
+  u32x4 qn[D / 32];
+};
+
+// One partition (a piece of a segment), bf16, through the carried rings; the
+// per-block work is that of run_piece_ring.  The waves are combined in the
+// region beside the rings (cmb), followed by the dummy KiB.
+template <int D, bool FUSE>
+__device__ void run_piece_stream(const DecodeArgs& a, const LogitXform& xf, const Piece& pc,
+                                 const Piece& nx, bool has_nx, RingStream<D>& rs, float* lds,
+                                 float* cmb) {
+  constexpr int KS = D / 32;                        // score products
+  constexpr int XT = D / 16;                        // output tiles
+  constexpr int kTileBytes = D * kBlock * 2;        // one block's K (or V)
+  constexpr int kRuns = 2 * kTileBytes / 1024;      // 1 KiB copies per block
+  constexpr int NS = kStreamRingBytes / (2 * kTileBytes);
+  static_assert(NS >= 2 && (NS & (NS - 1)) == 0, "a power of two, at least two blocks in flight");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c = lane & 15, j = lane >> 4;
+  const int G = a.gqa_group, Hkv = a.num_kv_heads, Hq = G * Hkv;
+  const int b = __builtin_amdgcn_readfirstlane(pc.b), g = __builtin_amdgcn_readfirstlane(pc.g);
+  const int j0 = __builtin_amdgcn_readfirstlane(pc.j0), j1 = __builtin_amdgcn_readfirstlane(pc.j1);
+  SeqSpan sp;
+  sp.first_blk = __builtin_amdgcn_readfirstlane(pc.sp.first_blk);
+  sp.nb = __builtin_amdgcn_readfirstlane(pc.sp.nb);
+  sp.vis_lo = __builtin_amdgcn_readfirstlane(pc.sp.vis_lo);
+  sp.L = __builtin_amdgcn_readfirstlane(pc.sp.L);
+  const int span = j1 - j0 - wave;
+  const int nw = span > 0 ? (span + kWaves - 1) / kWaves : 0;
+
+  // the carried state is the same in every lane: keep it scalar, so the ring
+  // addresses and the load descriptors stay scalar
+  has_nx = __builtin_amdgcn_readfirstlane((int)has_nx) != 0;
+  const bool pre = __builtin_amdgcn_readfirstlane((int)rs.pre) != 0;
+  const bool qpre = __builtin_amdgcn_readfirstlane((int)rs.qpre) != 0;
+  int nb_ = 0, ng = 0, nj0 = 0, nnw = 0, nfirst = 0;
+  if (has_nx) {
+    nb_ = __builtin_amdgcn_readfirstlane(nx.b);
+    ng = __builtin_amdgcn_readfirstlane(nx.g);
+    nj0 = __builtin_amdgcn_readfirstlane(nx.j0);
+    const int nj1 = __builtin_amdgcn_readfirstlane(nx.j1);
+    nfirst = __builtin_amdgcn_readfirstlane(nx.sp.first_blk);
+    const int nspan = nj1 - nj0 - wave;
+    nnw = nspan > 0 ? (nspan + kWaves - 1) / kWaves : 0;
+  }
+  const bool pf = has_nx && nnw >= NS;  // prefetch the next partition's first blocks
+
+  const int* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk + j0 + wave;
+  const int* nbt = a.block_tables + (size_t)nb_ * a.max_blocks_per_seq + nfirst + nj0 + wave;
+  int tbase = 0;
+  int tbl = pre ? rs.tbl : (lane < nw ? bt[kWaves * lane] : 0);
+  const int ntbl = pf && lane < nnw ? nbt[kWaves * lane] : 0;
+
+  u32x4 qf[KS];
+  if (qpre) {
+#pragma unroll
+    for (int s = 0; s < KS; ++s) qf[s] = rs.qn[s];
+  } else {
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * Hq + g * G + min(c, G - 1)) * D + 8 * j;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qf[s] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+  }
+  if (has_nx) {
+    const uint16_t* qrow =
+        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)nb_ * Hq + ng * G + min(c, G - 1)) * D + 8 * j;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      rs.qn[s] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+  }
+  NewToken<2, D> nt;
+  if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
+
+  f32x4 o[XT];
+#pragma unroll
+  for (int x = 0; x < XT; ++x) o[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = kNegInf, l_run = 0.f;
+  constexpr float kLazy = 8.0f;
+
+  const char* kpool = reinterpret_cast<const char*>(a.k_pool);
+  const char* vpool = reinterpret_cast<const char*>(a.v_pool);
+  char* ring = reinterpret_cast<char*>(lds) + wave * kStreamRingBytes;
+  char* dummy = reinterpret_cast<char*>(cmb) + combine_bytes<D>(G);
+  const int pos = __builtin_amdgcn_readfirstlane(rs.pos);
+  uint32_t okbits = __builtin_amdgcn_readfirstlane(rs.okbits);
+
+  // stream entry k of this partition: its block k, then (when prefetching)
+  // the next partition's blocks 0 .. NS - 1, then empty ranges (zeros).
+  // `fake`: an empty copy into the dummy KiB that takes no stream position.
+  auto issue = [&](int k, bool fake) {
+    int phys = 0, gg = g;
+    bool ok = false;
+    if (fake) {
+    } else if (k < nw) {
+      if (k - tbase >= 64) {  // uniform, every 64 blocks
+        tbase += 64;
+        tbl = tbase + lane < nw ? bt[kWaves * (tbase + lane)] : 0;
+      }
+      phys = __builtin_amdgcn_readlane(tbl, (k - tbase) & 63);
+      ok = (unsigned)phys < (unsigned)a.num_blocks;
+    } else if (pf && k - nw < NS) {
+      phys = __builtin_amdgcn_readlane(ntbl, (k - nw) & 63);
+      gg = ng;
+      ok = (unsigned)phys < (unsigned)a.num_blocks;
+    }
+    const size_t off = ((size_t)(ok ? phys : 0) * Hkv + gg) * kTileBytes;
+    const __amdgpu_buffer_rsrc_t rk = tile_range(kpool + off, ok ? kTileBytes : 0);
+    const __amdgpu_buffer_rsrc_t rv = tile_range(vpool + off, ok ? kTileBytes : 0);
+    const int slot = (pos + k) & (NS - 1);
+    if (!fake) okbits = (okbits & ~(1u << slot)) | ((uint32_t)ok << slot);
+    char* dst = fake ? dummy : ring + slot * 2 * kTileBytes;
+    const int step = fake ? 0 : 1024;  // a fake copy's runs all land on the dummy KiB
+#pragma unroll
+    for (int r = 0; r < kRuns / 2; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dst + r * step),
+                                               16, r * 1024 + lane * 16, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < kRuns / 2; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rv, (__attribute__((address_space(3))) void*)(dst + (fake ? 0 : kTileBytes) + r * step), 16,
+          r * 1024 + lane * 16, 0, 0, 0);
+  };
+
+  // NS prologue copies on every path (fake ones when the partition before
+  // issued this one's first blocks): the loop is then entered the same way
+  // whatever came before it, and its waits hold NS - 1 copies or more after
+  // each block.
+#pragma unroll
+  for (int k = 0; k < NS; ++k) issue(k, pre);
+  for (int i = 0; i < nw; ++i) {
+    // block i has landed: at least NS - 1 later stream entries were issued after it
+    constexpr int kAfter = (NS - 1) * kRuns;
+    __builtin_amdgcn_s_waitcnt((kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("" ::: "memory");
+    const int slot = (pos + i) & (NS - 1);
+    const bool ok = (okbits >> slot) & 1u;
+    const char* kt = ring + slot * 2 * kTileBytes;
+    const char* vt = kt + kTileBytes;
+    const int tok0 = (sp.first_blk + j0 + wave + kWaves * i) * kBlock;
+
+    u32x4 kf[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const u32x4*>(kt + (64 * s + lane) * 16);
+    const bool newtok = FUSE && nt.own && i == nw - 1;
+    if constexpr (FUSE)
+      if (newtok) nt.put_k(kf, lane);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = mma_bf16_k32(kf[s], qf[s], acc);
+    u32x2 vf[XT];
+#pragma unroll
+    for (int x = 0; x < XT; ++x)
+      vf[x] = *reinterpret_cast<const u32x2*>(vt + (16 * x + c) * 2 * kBlock + 8 * j);
+    if constexpr (FUSE) {
+      if (newtok) {
+        nt.put_v(vf, lane);
+        nt.store(lane);
+      }
+    }
+    mma_result_fence();
+
+    float s2[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = tok0 + 4 * j + r;
+      const bool vis = ok & (t >= sp.vis_lo) & (t < sp.L);
+      s2[r] = vis ? xf(acc[r]) : kNegInf;
+    }
+    float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+    mx = quad_max(mx);
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int x = 0; x < XT; ++x) o[x] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    float p[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s2[r] - m_use);
+    l_run += (p[0] + p[1]) + (p[2] + p[3]);
+    const u32x2 pa = {pack_bf16x2_hw(p[0], p[1]), pack_bf16x2_hw(p[2], p[3])};
+    if (tok0 + kBlock > sp.L) {  // tokens past the context may hold anything
+      const int nv = sp.L - tok0, t0 = 4 * j;
+      const uint32_t mlo = (t0 + 0 < nv ? 0x0000FFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
+      const uint32_t mhi = (t0 + 2 < nv ? 0x0000FFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+      for (int x = 0; x < XT; ++x) vf[x] = u32x2{vf[x].x & mlo, vf[x].y & mhi};
+    }
+#pragma unroll
+    for (int x = 0; x < XT; ++x) o[x] = mma_bf16_k16(vf[x], pa, o[x]);
+    asm volatile("" ::: "memory");
+    issue(i + NS, false);  // into the slot just read (the products have their operands)
+  }
+  // without a prefetch, let the copies past the end land (the next
+  // partition's prologue reuses the slots)
+  if (!pf) __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // ---- combine the four waves beside the rings ----
+  mma_result_fence();
+  const float l_tot = quad_sum(l_run);
+  float* lo = cmb;                    // [4][G][D]
+  float* lml = lo + kWaves * G * D;   // [4][G][2]
+  if (c < G) {
+#pragma unroll
+    for (int x = 0; x < XT; ++x)
+      *reinterpret_cast<f32x4*>(lo + ((size_t)wave * G + c) * D + 16 * x + 4 * j) = o[x];
+    if (j == 0) {
+      lml[(wave * G + c) * 2] = m_run;
+      lml[(wave * G + c) * 2 + 1] = l_tot;
+    }
+  }
+  __syncthreads();
+  combine_waves<true, D, false>(a, pc, lo, lml);
+  __syncthreads();  // the combine region is reused next
+
+  rs.pos = pos + nw;
+  rs.okbits = okbits;
+  rs.pre = pf;
+  rs.tbl = ntbl;
+  rs.qpre = has_nx;
+}
+
 // Output of a sequence with nothing to attend to: 0, lse = -inf.
 template <bool BF16, int D, bool V = false>
 __device__ void write_empty(const DecodeArgs& a, int b, int h_lo, int h_hi) {
@@ -958,17 +1247,17 @@ __device__ void write_empty(const DecodeArgs& a, int b, int h_lo, int h_hi) {
   }
 }
 
-// A piece of a split segment has stored its partial: count it in; the
+// k pieces of a split segment have stored their partials: count them in; the
 // workgroup that counts the last piece merges all of them into the output
 // and resets the counter (the counters start at zero and are left at zero).
 template <bool BF16, int D, bool V, typename SlotList>
-__device__ void finish_split(const DecodeArgs& a, int b, int g, SlotList slots, float* lds) {
+__device__ void finish_split(const DecodeArgs& a, int b, int g, SlotList slots, float* lds, int k = 1) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are done
   __syncthreads();
   int* cnt = a.seg_count + (size_t)b * a.num_kv_heads + g;
   int* flag = reinterpret_cast<int*>(lds);
   if (threadIdx.x == 0)
-    flag[0] = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == slots.count() - 1;
+    flag[0] = __hip_atomic_fetch_add(cnt, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == slots.count() - k;
   __syncthreads();
   const bool last = flag[0] != 0;
   __syncthreads();  // LDS is reused below
@@ -976,6 +1265,136 @@ __device__ void finish_split(const DecodeArgs& a, int b, int g, SlotList slots, 
   merge_segment<BF16, D, SlotList, V>(a, b, g, slots, lds);
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
+}
+
+// Split-K decode, persistent form (see run_piece_stream): workgroup w of N
+// takes items [w I / N, (w + 1) I / N) of the I (segment, partition) items.
+template <int D, bool FUSE>
+__global__ __launch_bounds__(kThreads, 1) void decode_fixed_stream_kernel(DecodeArgs a) {
+  extern __shared__ float lds[];
+  const LogitXform xf = make_xform(a.scale, a.softcap);
+  const int Hkv = a.num_kv_heads, G = a.gqa_group, B = a.num_seqs;
+  const int NP = a.num_partitions, PB = a.part_blocks;
+  const int N = gridDim.x, w = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  float* cmb = lds + kWaves * kStreamRingBytes / 4;
+  auto span = [&](int L) { return seq_span(L, a.window, a.max_context_len); };
+  // visible partitions of a sequence of length L
+  auto parts = [&](int L) -> int {
+    const SeqSpan sp = span(L);
+    return sp.nb > 0 ? (sp.first_blk + sp.nb - 1) / PB - sp.first_blk / PB + 1 : 0;
+  };
+
+  // context lengths of sequences 64 r + lane, r < kLenRegs, in registers
+  constexpr int kLenRegs = 4;
+  int Lr[kLenRegs];
+#pragma unroll
+  for (int r = 0; r < kLenRegs; ++r) {
+    const int b = r * kWave + lane;
+    Lr[r] = b < B ? a.context_lens[b] : 0;
+  }
+  auto len_at = [&](int r) -> int {  // length of sequence 64 r + lane (0 past B)
+    int L = 0;
+#pragma unroll
+    for (int q = 0; q < kLenRegs; ++q) L = q == r ? Lr[q] : L;
+    if (r >= kLenRegs) {
+      const int b = r * kWave + lane;
+      L = b < B ? a.context_lens[b] : 0;
+    }
+    return L;
+  };
+  auto len_of = [&](int b) -> int {  // length of sequence b (uniform)
+    return b < kLenRegs * kWave ? __builtin_amdgcn_readlane(len_at(b / kWave), b % kWave)
+                                : a.context_lens[b];
+  };
+
+  for (int b = w; b < B; b += N)  // sequences with no visible token
+    if (span(len_of(b)).nb == 0) write_empty<true, D, false>(a, b, 0, Hkv * G);
+
+  long long I = 0;
+  for (int r = 0; r * kWave < B; ++r) I += wave_sum_i64(parts(len_at(r)));
+  I *= Hkv;
+  const long long i0 = __builtin_amdgcn_readfirstlane((long long)w * I / N);
+  const long long i1 = (long long)(w + 1) * I / N;
+  if (i0 >= i1) return;
+
+  // segment holding item i0: first sequence whose inclusive prefix exceeds i0
+  long long run = 0, seg_base = 0;
+  int b0 = 0;
+  for (int r = 0; r * kWave < B; ++r) {
+    const long long nph = (long long)parts(len_at(r)) * Hkv;
+    const long long incl = wave_incl_scan_i64(nph, lane);
+    const unsigned long long hit = __ballot(run + incl > i0);
+    if (hit) {
+      const int l0 = __ffsll(hit) - 1;
+      b0 = r * kWave + l0;
+      seg_base = run + __shfl(incl - nph, l0);
+      break;
+    }
+    run += __shfl(incl, kWave - 1);
+  }
+  seg_base = __builtin_amdgcn_readfirstlane(seg_base);
+
+  // The pieces of [i0, i1): runs of consecutive partitions of one segment.
+  // A run is walked as one piece (its partitions' partials are folded as the
+  // blocks stream: the online softmax over a run of partitions is the
+  // log-sum-exp merge of their partials) and stored at the slot of its first
+  // partition.  Cursor: sequence cb, kv head cg, partition index cp (from the
+  // first visible one) and the segment's first item S.
+  int cb = b0;
+  SeqSpan csp = span(len_of(cb));
+  int cnp = parts(csp.L);
+  const int r0 = (int)(i0 - seg_base);
+  int cg = r0 / cnp, cp = r0 % cnp;
+  long long S = seg_base + (long long)cg * cnp;
+  long long left = i1 - i0;
+  auto next_piece = [&](Piece& out) -> bool {
+    if (left <= 0) return false;
+    const int run_len = (int)min((long long)(cnp - cp), left);
+    const int p_lo = csp.first_blk / PB, p = p_lo + cp;
+    const int lo = max(p * PB, csp.first_blk);
+    const int hi = min((p + run_len) * PB, csp.first_blk + csp.nb);
+    out.b = cb;
+    out.g = cg;
+    out.sp = csp;
+    out.j0 = lo - csp.first_blk;
+    out.j1 = hi - csp.first_blk;
+    out.slot = (cb * Hkv + cg) * NP + p;
+    out.S = S;
+    left -= run_len;
+    cp += run_len;
+    if (left > 0) {  // the run ended with its segment: move to the next one
+      S += cnp;
+      cp = 0;
+      if (++cg == Hkv) {
+        cg = 0;
+        do {
+          ++cb;
+          csp = span(len_of(cb));
+          cnp = parts(csp.L);
+        } while (cnp == 0);
+      }
+    }
+    return true;
+  };
+
+  RingStream<D> rs;
+  Piece cur;
+  bool has = __builtin_amdgcn_readfirstlane((int)next_piece(cur)) != 0;
+  while (has) {
+    Piece nxt = cur;
+    const bool has_n = __builtin_amdgcn_readfirstlane((int)next_piece(nxt)) != 0;
+    run_piece_stream<D, FUSE>(a, xf, cur, nxt, has_n, rs, lds, cmb);
+    if (!(cur.j0 == 0 && cur.j1 == cur.sp.nb)) {
+      const int seg = cur.b * Hkv + cur.g;
+      const int p_lo = cur.sp.first_blk / PB;
+      const long long nparts = parts(cur.sp.L);
+      finish_split<true, D, false>(a, cur.b, cur.g,
+                                   RunSlots{I, cur.S, cur.S + nparts, N, seg * NP + p_lo}, cmb);
+    }
+    cur = nxt;
+    has = has_n;
+  }
 }
 
 template <bool BF16, int D, bool FIXED, bool FUSE, bool EVICT>
@@ -1183,9 +1602,21 @@ hipError_t launch_d(DecodeArgs a, hipStream_t stream) {
   size_t lds = (size_t)kWaves * a.gqa_group * (D + 2) * sizeof(float);  // the waves' combine
   lds = std::max(lds, (size_t)(4 * kThreads + 2 * 16) * sizeof(float));  // a merge
   if (BF16 && kRingForm<D>) lds = std::max(lds, (size_t)kWaves * kRingBytesPerWave<D>);
-  if (a.part_blocks > 0)
+  if (a.part_blocks > 0) {
+    if constexpr (BF16 && kRingForm<D>) {
+      if (PKV_DECODE_FIXED_STREAM && fixed_stream_lds<D>(a.gqa_group) <= kLdsPerCu) {
+        // persistent form: one workgroup per CU, at most one per item
+        DecodeArgs p = a;
+        const long long items = (long long)a.num_seqs * a.num_kv_heads * a.num_partitions;
+        p.num_workers = (int32_t)std::max(1LL, std::min((long long)a.cu_count, items));
+        const size_t pl = (size_t)fixed_stream_lds<D>(a.gqa_group);
+        return a.k_new ? launch_k(decode_fixed_stream_kernel<D, true>, p, pl, stream)
+                       : launch_k(decode_fixed_stream_kernel<D, false>, p, pl, stream);
+      }
+    }
     return a.k_new ? launch_k(decode_kernel<BF16, D, true, true, false>, a, lds, stream)
                    : launch_k(decode_kernel<BF16, D, true, false, false>, a, lds, stream);
+  }
   if (a.scores) {  // balanced split with per-head logits, then the column mass
     hipError_t e = launch_k(decode_kernel<BF16, D, false, false, true>, a, lds, stream);
     if (e != hipSuccess || a.column_mass == nullptr) return e;
