@@ -767,14 +767,15 @@ __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const 
   __syncthreads();  // LDS is reused by the next piece
 }
 
-// LDS bytes of the ring each wave of the LDS form streams its blocks through
-// (two blocks of 16 KiB at head_dim 256), and workgroups per CU: at head_dim
-// <= 128 two workgroups share a CU (16 KiB rings, 2 or 4 blocks in flight per
-// wave), so one's start-up overlaps the other's streaming.
+// LDS bytes of the ring each wave of the LDS form streams its blocks through,
+// and workgroups per CU: 32 KiB rings and one workgroup per CU at head_dim
+// 128 and 256 (four and two blocks in flight per wave); at head_dim 64 two
+// workgroups share a CU (16 KiB rings, four blocks in flight per wave), so
+// one's start-up overlaps the other's streaming.
 template <int D>
-constexpr int kRingBytesPerWave = D >= 256 ? 32768 : 16384;
+constexpr int kRingBytesPerWave = D >= 128 ? 32768 : 16384;
 template <int D>
-constexpr int kRingWgsPerCu = D >= 256 ? 1 : 2;
+constexpr int kRingWgsPerCu = D >= 128 ? 1 : 2;
 
 // The balanced split's price of one piece (its start, partial store and
 // merge), in cache blocks of one kv head: PKV_DECODE_PIECE_COST_BYTES of K/V.
