@@ -355,9 +355,9 @@ def time_copy_blocks(bench, iters, torch):
 def time_mixed(torch, pkv, wl, iters=20):
     """A mixed batch: 4 prefill chunks (2048 cached + 512 new tokens) and 28
     decode rows (contexts uniform in [512, 4096]), 8 q / 2 kv heads, D 256,
-    bf16.  Times paged_attn_mixed (chunks through the prefill kernel, decode
-    rows through the balanced decode split) and, for comparison, the same
-    batch through one prefill launch."""
+    bf16.  Times paged_attn_mixed (one launch: the chunks through the prefill
+    body, the decode rows through the balanced decode split beside them) and,
+    for comparison, the same batch through one prefill launch."""
     import numpy as np
 
     rng = np.random.default_rng(6)

@@ -123,7 +123,7 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const Deco
                 int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
                 int32_t block_size, float scale, float softcap, int32_t window,
                 int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
-                hipStream_t stream) {
+                hipStream_t stream, pkv::DecodeArgs* build_only = nullptr) {
   int rc = check_common(fn, out, lse, q, k_pool, v_pool, num_blocks, block_tables,
                         max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
                         gqa_group, head_dim, block_size, scale, softcap, dtype);
@@ -195,6 +195,10 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const Deco
     a.part_blocks = 0;
     a.num_partitions = 0;
     a.num_workers = 0;  // chosen by launch_decode for the kernel variant
+  }
+  if (build_only) {
+    *build_only = a;
+    return PKV_OK;
   }
   return from_hip(pkv::launch_decode(a, head_dim, dtype == PKV_BF16, stream), fn);
 }
@@ -385,14 +389,18 @@ int paged_attn_decode_sink_h2o(void* out, float* lse, const void* q, const void*
                      workspace_bytes, dtype, reinterpret_cast<hipStream_t>(stream));
 }
 
-int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q_lens,
-                       int32_t num_q_tokens, int32_t max_q_len, const void* k_pool,
-                       const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
-                       int32_t max_blocks_per_seq, const int32_t* context_lens,
-                       int32_t max_context_len, int32_t num_seqs, int32_t num_kv_heads,
-                       int32_t gqa_group, int32_t head_dim, int32_t block_size, float scale,
-                       float softcap, int32_t window, int32_t dtype, struct ihipStream_t* stream) {
-  const char* fn = "paged_attn_prefill";
+}  // extern "C"
+
+// Checks a prefill call and fills its kernel arguments; *empty is set when
+// there is nothing to compute (the call is then a no-op).
+int prefill_build(const char* fn, void* out, float* lse, const void* q, const int32_t* cu_q_lens,
+                  int32_t num_q_tokens, int32_t max_q_len, const void* k_pool, const void* v_pool,
+                  int32_t num_blocks, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, int32_t max_context_len, int32_t num_seqs,
+                  int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim, int32_t block_size,
+                  float scale, float softcap, int32_t window, int32_t dtype, pkv::PrefillArgs* out_a,
+                  bool* empty) {
+  *empty = true;
   int rc = check_common(fn, out, lse, q, k_pool, v_pool, num_blocks, block_tables,
                         max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
                         gqa_group, head_dim, block_size, scale, softcap, dtype);
@@ -408,7 +416,8 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q
   if (!cu_q_lens || !aligned(cu_q_lens, 4))
     return fail(PKV_EINVAL, "%s: cu_q_lens null or misaligned", fn);
 
-  pkv::PrefillArgs a{};
+  pkv::PrefillArgs& a = *out_a;
+  a = pkv::PrefillArgs{};
   a.out = out;
   a.lse = lse;
   a.q = q;
@@ -431,6 +440,27 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q
   const long long items = (long long)num_seqs * num_kv_heads * a.tiles_per_seq;
   if (items > INT_MAX) return fail(PKV_EINVAL, "%s: %lld work items exceed the grid limit", fn, items);
   a.num_items = (int32_t)items;
+  *empty = false;
+  return PKV_OK;
+}
+
+extern "C" {
+
+int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q_lens,
+                       int32_t num_q_tokens, int32_t max_q_len, const void* k_pool,
+                       const void* v_pool, int32_t num_blocks, const int32_t* block_tables,
+                       int32_t max_blocks_per_seq, const int32_t* context_lens,
+                       int32_t max_context_len, int32_t num_seqs, int32_t num_kv_heads,
+                       int32_t gqa_group, int32_t head_dim, int32_t block_size, float scale,
+                       float softcap, int32_t window, int32_t dtype, struct ihipStream_t* stream) {
+  const char* fn = "paged_attn_prefill";
+  pkv::PrefillArgs a;
+  bool empty = true;
+  const int rc = prefill_build(fn, out, lse, q, cu_q_lens, num_q_tokens, max_q_len, k_pool, v_pool,
+                               num_blocks, block_tables, max_blocks_per_seq, context_lens,
+                               max_context_len, num_seqs, num_kv_heads, gqa_group, head_dim,
+                               block_size, scale, softcap, window, dtype, &a, &empty);
+  if (rc != PKV_OK || empty) return rc;
   return from_hip(pkv::launch_prefill(a, head_dim, dtype == PKV_BF16,
                                       reinterpret_cast<hipStream_t>(stream)),
                   fn);
@@ -455,6 +485,31 @@ int paged_attn_mixed(void* out, float* lse, const void* q, const int32_t* cu_q_l
   const int32_t P = num_prefill_seqs, Bd = num_seqs - num_prefill_seqs;
   const size_t row = (size_t)num_kv_heads * gqa_group * head_dim * es;  // one q / out row
   int rc = PKV_OK;
+  char* o = static_cast<char*>(out) + (size_t)num_prefill_tokens * row;
+  const char* qd = static_cast<const char*>(q) + (size_t)num_prefill_tokens * row;
+  float* ld = lse ? lse + (size_t)num_prefill_tokens * num_kv_heads * gqa_group : nullptr;
+  if (P > 0 && Bd > 0 && dtype == PKV_BF16) {
+    // both parts in one launch
+    pkv::PrefillArgs pa;
+    bool empty = true;
+    rc = prefill_build(fn, out, lse, q, cu_q_lens, num_prefill_tokens, max_q_len, k_pool, v_pool,
+                       num_blocks, block_tables, max_blocks_per_seq, context_lens,
+                       max_context_len, P, num_kv_heads, gqa_group, head_dim, block_size, scale,
+                       softcap, window, dtype, &pa, &empty);
+    if (rc != PKV_OK) return rc;
+    pkv::DecodeArgs da;
+    rc = decode_impl(fn, o, ld, qd, DecodeExtras{}, k_pool, v_pool, num_blocks,
+                     block_tables + (size_t)P * max_blocks_per_seq, max_blocks_per_seq,
+                     context_lens + P, max_context_len, Bd, num_kv_heads, gqa_group, head_dim,
+                     block_size, scale, softcap, window, 0, workspace, workspace_bytes, dtype,
+                     reinterpret_cast<hipStream_t>(stream), &da);
+    if (rc != PKV_OK) return rc;
+    if (!empty)
+      return from_hip(pkv::launch_mixed(pa, da, head_dim, reinterpret_cast<hipStream_t>(stream)),
+                      fn);
+    return from_hip(pkv::launch_decode(da, head_dim, true, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+  }
   if (P > 0) {
     rc = paged_attn_prefill(out, lse, q, cu_q_lens, num_prefill_tokens, max_q_len, k_pool, v_pool,
                             num_blocks, block_tables, max_blocks_per_seq, context_lens,
@@ -463,9 +518,6 @@ int paged_attn_mixed(void* out, float* lse, const void* q, const int32_t* cu_q_l
     if (rc != PKV_OK) return rc;
   }
   if (Bd > 0) {
-    char* o = static_cast<char*>(out) + (size_t)num_prefill_tokens * row;
-    const char* qd = static_cast<const char*>(q) + (size_t)num_prefill_tokens * row;
-    float* ld = lse ? lse + (size_t)num_prefill_tokens * num_kv_heads * gqa_group : nullptr;
     rc = decode_impl(fn, o, ld, qd, DecodeExtras{}, k_pool, v_pool, num_blocks,
                      block_tables + (size_t)P * max_blocks_per_seq, max_blocks_per_seq,
                      context_lens + P, max_context_len, Bd, num_kv_heads, gqa_group, head_dim,

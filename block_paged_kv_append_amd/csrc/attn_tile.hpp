@@ -27,6 +27,10 @@
 
 namespace pkv {
 
+// Workgroup shape of the attention kernels: four waves of 64 lanes.
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+
 // Wait states between a matrix-core result and its first reader.  The
 // compiler's hazard padding does not always reach a read that follows the
 // last matrix op across a branch (seen on gfx950: an accumulator read two

@@ -55,8 +55,6 @@ constexpr bool kRingForm = !PKV_DECODE_REGISTER_FORM;
 namespace pkv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
 
 // Partial results pass between workgroups (possibly on different XCDs, whose
 // L2 caches are not coherent with each other) only through device-scope
@@ -1398,9 +1396,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fixed_stream_kernel(Decode
   }
 }
 
+// The decode of workgroup `blk` (of num_workers in the balanced split, of
+// the (segment, partition) grid in the fixed one), with `lds` the
+// workgroup's dynamic LDS.  decode_kernel runs it for its own workgroup; the
+// mixed-batch kernel runs it for the workgroups after the prefill's.
 template <bool BF16, int D, bool FIXED, bool FUSE, bool EVICT>
-__global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<D> : 2) void decode_kernel(DecodeArgs a) {
-  extern __shared__ float lds[];
+__device__ __forceinline__ void decode_body(const DecodeArgs& a, int blk, float* lds) {
   auto run_one = [&](const LogitXform& xf, const Piece& pc) {
     if constexpr (BF16) {
       if constexpr (kRingForm<D>)
@@ -1423,7 +1424,7 @@ __global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<
 
   if constexpr (FIXED) {
     const int NP = a.num_partitions, PB = a.part_blocks;
-    const int seg = blockIdx.x / NP, p = blockIdx.x % NP;
+    const int seg = blk / NP, p = blk % NP;
     const int b = seg / Hkv, g = seg % Hkv;
     Piece pc;
     pc.b = b;
@@ -1446,7 +1447,7 @@ __global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<
       finish_split<BF16, D, EVICT>(a, b, g, SplitSlots{seg * NP, p_lo, p_hi}, lds);
     }
   } else {
-    const int N = a.num_workers, w = blockIdx.x;
+    const int N = a.num_workers, w = blk;
     const int lane = threadIdx.x & 63;
     const int B = a.num_seqs;
 
@@ -1540,6 +1541,12 @@ __global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<
       }
     }
   }
+}
+
+template <bool BF16, int D, bool FIXED, bool FUSE, bool EVICT>
+__global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<D> : 2) void decode_kernel(DecodeArgs a) {
+  extern __shared__ float lds[];
+  decode_body<BF16, D, FIXED, FUSE, EVICT>(a, blockIdx.x, lds);
 }
 
 // H2O statistic of the decode step: mass[b, g, t] = sum over the group's
@@ -1641,9 +1648,11 @@ hipError_t launch_dt(const DecodeArgs& a, int head_dim, hipStream_t stream) {
 
 }  // namespace
 
+#ifndef PKV_ATTN_BODIES_ONLY
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream) {
   if (a.num_seqs <= 0) return hipSuccess;
   return bf16 ? launch_dt<true>(a, head_dim, stream) : launch_dt<false>(a, head_dim, stream);
 }
+#endif
 
 }  // namespace pkv

@@ -109,6 +109,10 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, hipStream_t stream);
+// a mixed batch in one launch (bf16): the prefill of pa's chunks, then the
+// balanced decode of da's rows (da.num_workers is chosen here)
+hipError_t launch_mixed(const PrefillArgs& pa, const DecodeArgs& da, int head_dim,
+                        hipStream_t stream);
 
 // Row tiles (of 16 GQA-packed query rows) per wave in the prefill kernel.
 int prefill_row_tiles(int head_dim, bool bf16);

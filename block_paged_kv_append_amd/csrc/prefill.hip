@@ -28,8 +28,6 @@
 namespace pkv {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWaves = 4;
 
 template <bool BF16, int D, int RT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
@@ -253,8 +251,18 @@ __device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int byte_o
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)wave_dst, 16, byte_off, 0, 0, 0);
 }
 
+// LDS of the matrix-core prefill: NB stages of K and V runs
+template <int D, int NB>
+constexpr int kPrefillStageU4 = (D / 16 + 2 * (D / 32)) * kWave;
+template <int D, int NB>
+constexpr size_t kPrefillLdsBytes = (size_t)NB * kPrefillStageU4<D, NB> * 16;
+
+// The prefill of work item `blk` (before the XCD-aware renumbering), with
+// `smem` its stage ring in LDS.  prefill_mma32_kernel runs it for its own
+// workgroup; the mixed-batch kernel runs it for the first workgroups of its
+// grid.
 template <int D, int NB, bool SC>
-__global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs a) {
+__device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk, u32x4* smem) {
   constexpr int KD = D / 16;                    // K runs per stage = QK products
   constexpr int XT = D / 32;                    // output row tiles of O^T
   constexpr int kRuns = KD + 2 * XT;            // 1 KiB runs per stage
@@ -265,7 +273,6 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
   constexpr int kTileU4 = D * kBlock * 2 / 16;  // chunks of one block's K (or V) in the pool
   static_assert(KD % kWaves == 0 && (2 * XT) % kWaves == 0, "runs must split over the waves");
   static_assert(NB >= 3 && (NB & (NB - 1)) == 0, "ring of 4 or 8 stages");
-  __shared__ u32x4 smem[NB * kStageU4];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -274,8 +281,8 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
   const int PPW = 32 / G;  // positions per wave
   const LogitXform xf = make_xform(a.scale, a.softcap);
 
-  int item = blockIdx.x;
-  if (a.num_items % 8 == 0) item = (blockIdx.x % 8) * (a.num_items / 8) + blockIdx.x / 8;
+  int item = blk;
+  if (a.num_items % 8 == 0) item = (int)((unsigned)blk % 8u) * (a.num_items / 8) + (int)((unsigned)blk / 8u);
   const int tile = item % a.tiles_per_seq;
   const int bg = item / a.tiles_per_seq;
   const int g = bg % Hkv, b = bg / Hkv;
@@ -588,6 +595,12 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
                 pack_bf16x2_hw(o[x][4 * h + 2] * inv, o[x][4 * h + 3] * inv)};
 }
 
+template <int D, int NB, bool SC>
+__global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs a) {
+  __shared__ u32x4 smem[NB * kPrefillStageU4<D, NB>];
+  prefill_mma32_body<D, NB, SC>(a, blockIdx.x, smem);
+}
+
 template <int D>
 void launch_mma32(PrefillArgs a, hipStream_t stream) {
   if (a.softcap > 0.f)
@@ -607,6 +620,7 @@ hipError_t launch_p(PrefillArgs a, hipStream_t stream) {
 
 }  // namespace
 
+#ifndef PKV_ATTN_BODIES_ONLY
 // Row tiles per wave of the bf16 (LDS) form, and of the fp32 form.
 int prefill_row_tiles(int head_dim, bool bf16) {
   if (bf16) return 2;  // 32 rows per wave
@@ -633,5 +647,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, hipStre
   }
   return hipErrorInvalidValue;
 }
+
+#endif
 
 }  // namespace pkv

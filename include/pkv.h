@@ -362,9 +362,12 @@ int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q
  * rows: one query each, rows num_prefill_tokens + (b - num_prefill_seqs).
  * block_tables / context_lens cover all num_seqs sequences in that order.
  * The result is that of paged_attn_prefill over the whole batch (a decode row
- * is a one-row chunk), but the chunks run through the prefill kernel and the
- * decode rows through the balanced decode split, which spreads a long row
- * over every compute unit (two launches on `stream`).
+ * is a one-row chunk), but the chunks run through the matrix-core prefill and
+ * the decode rows through the balanced decode split, which spreads a long row
+ * over several compute units.  For bf16 with both parts present this is one
+ * launch on `stream`: the chunks' workgroups first in the grid, the decode
+ * rows' after them, sized to the compute units the chunks leave free; fp32,
+ * or a batch with only one part, runs that part's own kernel.
  *   out, q, lse   [num_prefill_tokens + num_seqs - num_prefill_seqs, Hq, D]
  *   workspace     >= paged_attn_decode_workspace_size(num_seqs -
  *                 num_prefill_seqs, ..., 0) bytes when there are decode rows
