@@ -18,7 +18,7 @@ import torch
 import block_paged_kv_append_amd as pkv
 import oracle
 from block_paged_kv_append_amd import workloads as wl
-from tests.gpu_common import (check_close, check_lse, dev, i32, oracle_decode, run_append,
+from tests.gpu_common import (as_f64, check_close, check_lse, dev, i32, oracle_decode, run_append,
                               run_decode, run_prefill)
 
 pytestmark = pytest.mark.gpu
@@ -167,19 +167,20 @@ def test_decode_more_workgroups_than_blocks():
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("B", [65, 300])
-def test_decode_large_batch(B):
-    """Batches past one wave of lengths (65) and past the lengths the balanced
-    split holds in registers (300: sequences 256 and up are read as needed),
-    with empty sequences among them."""
+@pytest.mark.parametrize("mode,P", [("balanced", None), ("splitk", 32)])
+def test_decode_large_batch(B, mode, P):
+    """Batches past one wave of lengths (65) and past the lengths the decode
+    holds in registers (300: sequences 256 and up are read as needed), with
+    empty sequences among them, in the balanced and the split-K form."""
     rng = np.random.default_rng(360 + B)
     lens = rng.integers(0, 200, size=B)
     lens[rng.choice(B, size=5, replace=False)] = 0
     case = wl.make_decode_case(361 + B, [int(x) for x in lens], 8, 2, 64, "bf16", softcap=30.0)
-    banner("decode large batch", B)
-    out, lse = run_decode(case)
+    banner("decode large batch", B, mode)
+    out, lse = run_decode(case, mode, P)
     ref, ref_lse = oracle_decode(case)
-    check_close(out, ref, "bf16", f"B={B}")
-    check_lse(lse, ref_lse, f"B={B}")
+    check_close(out, ref, "bf16", f"B={B} {mode}")
+    check_lse(lse, ref_lse, f"B={B} {mode}")
 
 
 # ---------------------------------------------------------------------------
@@ -344,3 +345,62 @@ def test_mixed_call_chunks_then_decode_rows(D, cap, W):
                                   case.context_lens, case.scale, case.softcap, case.window, "bf16")
     check_close(out.float().cpu().numpy().astype(np.float64), ref, "bf16", "mixed call")
     check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, "mixed call")
+
+
+def _mixed_call(case, P, dtype, ws=None):
+    """paged_attn_mixed over the case's batch: its first P sequences are
+    chunks, the rest one-row decode rows (their K/V already appended)."""
+    kp, vp = run_append(case)
+    q = dev(case.q, dtype)
+    out = torch.full_like(q, float("nan"))
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    cu = case.cu_q_lens[:P + 1]
+    max_q = int(np.diff(cu).max())
+    pkv.paged_attn_mixed(out, q, i32(cu), int(cu[-1]), max_q, kp, vp, i32(case.block_tables),
+                         i32(case.context_lens), case.max_context_len, case.scale, case.softcap,
+                         case.window, lse=lse, workspace=ws)
+    torch.cuda.synchronize()
+    return as_f64(out), lse.cpu().numpy().astype(np.float64)
+
+
+def _mixed_ref(case, dtype):
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           dtype)
+    return oracle.prefill(case.q, case.cu_q_lens, kr, vr, case.block_tables, case.context_lens,
+                          case.scale, case.softcap, case.window, dtype)
+
+
+@pytest.mark.gpu
+def test_mixed_call_bench_batch_full():
+    """The bench's mixed batch at full size: 4 chunks of 512 new tokens on 2048
+    cached ones and 28 decode rows with contexts uniform in [512, 4096], 8 q /
+    2 kv heads, D 256, softcap 50, in one launch; twice on one workspace (the
+    launch leaves the decode's counters at zero)."""
+    rng = np.random.default_rng(6)
+    lens = rng.integers(512, 4097, size=28)
+    cached = [2048] * 4 + [int(L) - 1 for L in lens]
+    chunk = [512] * 4 + [1] * 28
+    case = wl.make_prefill_case(6, cached, chunk, 8, 2, 256, "bf16", scale=1.0 / 16.0, softcap=50.0)
+    ref, ref_lse = _mixed_ref(case, "bf16")
+    ws = torch.zeros(pkv.paged_attn_decode_workspace_size(28, 2, 4, 256, case.max_context_len, 0),
+                     dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        banner("mixed bench batch", rep)
+        out, lse = _mixed_call(case, 4, "bf16", ws)
+        check_close(out, ref, "bf16", f"mixed bench batch {rep}")
+        check_lse(lse, ref_lse, f"mixed bench batch {rep}")
+    assert int(ws[:4 * 56].view(torch.int32).abs().sum()) == 0  # counters back at zero
+
+
+@pytest.mark.gpu
+def test_mixed_call_fp32():
+    """fp32 pools take the two-launch form of paged_attn_mixed."""
+    cached = [100, 40, 300, 17, 0]
+    chunk = [50, 24, 1, 1, 1]
+    case = wl.make_prefill_case(497, cached, chunk, 4, 1, 64, "f32", softcap=20.0)
+    banner("mixed fp32")
+    out, lse = _mixed_call(case, 2, "f32")
+    ref, ref_lse = _mixed_ref(case, "f32")
+    check_close(out, ref, "f32", "mixed fp32")
+    check_lse(lse, ref_lse, "mixed fp32")
+
