@@ -491,7 +491,7 @@ def cpu_baseline(case, budget_s):
 def main():
     args = parse_args()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: the path runs on one GPU; --gpus {args.gpus} is not supported "
               f"(use --gpus 1)", file=sys.stderr)
         sys.exit(2)
     import numpy as np

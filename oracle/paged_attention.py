@@ -28,7 +28,7 @@ block table into contiguous arrays, then apply the textbook definition
 softmax(scale * q k^T) v over the visible keys.  Everything is evaluated in
 float64 on the exact values stored in bf16 / fp32.
 
-Readings taken where the pages are silent (each is listed in the design doc too):
+Readings taken where the pages are silent:
 
 * pool layout "vLLM/PagedAttention" [inside]: K pool
   ``[NB, Hkv, D/X, 16, X]`` (X = elements per 16 bytes), V pool
