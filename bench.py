@@ -404,26 +404,6 @@ def time_mixed(torch, pkv, wl, iters=20):
     return res[0], res[1]
 
 
-def read_rate(torch) -> float:
-    """GB/s of a plain read of 1 GiB right now (torch.sum over fp32: a library
-    reduction, read-bound): the read bandwidth this GPU delivers to a simple
-    kernel, the practical ceiling beside the 8 TB/s nominal peak."""
-    n = 1 << 28  # fp32 elements: 1 GiB
-    x = torch.ones(n, dtype=torch.float32, device="cuda")
-    for _ in range(5):
-        x.sum()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(20):
-        x.sum()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 20
-    del x
-    torch.cuda.empty_cache()
-    return 4 * n / (ms * 1e-3) / 1e9
-
-
 def copy_rate(torch) -> float:
     """GB/s (bytes read + written) of a plain 1 GiB device copy right now: the
     bandwidth this GPU delivers to a trivial kernel, as context for the rates
@@ -603,7 +583,6 @@ def main():
 
     if not args.quick:
         line["box_copy_gbs"] = round(copy_rate(torch), 1)
-        line["box_read_gbs"] = round(read_rate(torch), 1)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
