@@ -205,9 +205,14 @@ int paged_attn_decode(void* out, float* lse, const void* q, const void* k_pool,
  * paged_attn_decode_splitk -- the split-K decode variant (page "Inference
  * Server", section "The engine").  Sequence b's tokens are cut into
  * partitions [p * partition_size, (p + 1) * partition_size), anchored at
- * token 0; each partition yields (max logit, sum of exponentials, partial
- * output) and the partitions are merged by log-sum-exp.  Arguments as
- * paged_attn_decode, plus
+ * token 0; each partition's (max logit, sum of exponentials, partial output)
+ * enters a log-sum-exp merge.  The partitions are the units of work: each
+ * workgroup (one per compute unit) takes a run of consecutive partitions,
+ * folds those of one sequence and kv head as their blocks stream (the online
+ * softmax over a run is the log-sum-exp merge of its partitions' partials)
+ * and stores one partial per run; the runs are merged by log-sum-exp in the
+ * same launch.  The result equals the partition-by-partition merge up to
+ * rounding order.  Arguments as paged_attn_decode, plus
  *   partition_size  tokens per partition, a positive multiple of 16
  *   workspace       >= paged_attn_decode_workspace_size(..., partition_size)
  */
