@@ -211,8 +211,11 @@ int paged_attn_decode(void* out, float* lse, const void* q, const void* k_pool,
  * folds those of one sequence and kv head as their blocks stream (the online
  * softmax over a run is the log-sum-exp merge of its partitions' partials)
  * and stores one partial per run; the runs are merged by log-sum-exp in the
- * same launch.  The result equals the partition-by-partition merge up to
- * rounding order.  Arguments as paged_attn_decode, plus
+ * same launch.  (Where that form's LDS does not fit -- bf16 with a GQA group
+ * of 8 or more at head_dim 256, or 16 at head_dim 128 -- and for fp32, each
+ * partition is a workgroup of its own.)  The result equals the
+ * partition-by-partition merge up to rounding order.  Arguments as
+ * paged_attn_decode, plus
  *   partition_size  tokens per partition, a positive multiple of 16
  *   workspace       >= paged_attn_decode_workspace_size(..., partition_size)
  */
