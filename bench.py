@@ -404,6 +404,45 @@ def time_mixed(torch, pkv, wl, iters=20):
     return res[0], res[1]
 
 
+def time_eviction(torch, pkv, wl):
+    """The decode behind the eviction policies, beside the plain decode of the
+    same workload: AttentionSink (4 sink tokens kept beside the 512-token
+    window) on the sliding-window workload, and H2O (per-head logits, then the
+    per-token attention mass of the step) on the Gemma-style workload."""
+    res = {}
+    c = wl.sliding_window_decode()
+    b = DecodeBench(c, 0, torch, pkv)
+
+    def sink(r):
+        pkv.paged_attn_decode_sink_h2o(b.out, b.q, b.kp, b.vp, b.bt[r], b.cl, c.max_context_len,
+                                       c.scale, c.softcap, c.window, sink_tokens=4, workspace=b.ws)
+
+    res["attention_sink"] = {"workload": "sliding_window_decode + 4 sink tokens",
+                             "ms": round(time_decode_op(b, 20, torch, sink), 5),
+                             "plain_decode_ms": round(time_decode_op(b, 20, torch), 5)}
+    del b, c
+    torch.cuda.empty_cache()
+    c = wl.gemma_decode()
+    b = DecodeBench(c, 0, torch, pkv)
+    S = (c.max_context_len + 15) // 16 * 16  # logit rows: a multiple of 16 >= the longest context
+    scores = torch.empty(c.num_seqs, c.num_q_heads, S, device="cuda")
+    mass = torch.empty(c.num_seqs, c.num_kv_heads, S, device="cuda")
+    lse = torch.empty(c.num_seqs, c.num_q_heads, device="cuda")
+
+    def h2o(r):
+        pkv.paged_attn_decode_sink_h2o(b.out, b.q, b.kp, b.vp, b.bt[r], b.cl, c.max_context_len,
+                                       c.scale, c.softcap, 0, scores=scores, column_mass=mass,
+                                       lse=lse, workspace=b.ws)
+
+    res["h2o_column_mass"] = {"workload": "gemma_decode: logits [32, 8, %d] and mass [32, 2, %d]"
+                                          % (S, S),
+                              "ms": round(time_decode_op(b, 20, torch, h2o), 5),
+                              "plain_decode_ms": round(time_decode_op(b, 20, torch), 5)}
+    del b, c, scores, mass
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_rate(torch) -> float:
     """GB/s (bytes read + written) of a plain 1 GiB device copy right now: the
     bandwidth this GPU delivers to a trivial kernel, as context for the rates
@@ -580,6 +619,7 @@ def main():
             del b, c
             torch.cuda.empty_cache()
         line["other_workloads"] = extra
+        line["eviction_policies"] = time_eviction(torch, pkv, wl)
 
     if not args.quick:
         line["box_copy_gbs"] = round(copy_rate(torch), 1)
