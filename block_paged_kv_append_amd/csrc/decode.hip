@@ -765,6 +765,82 @@ __device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const 
   __syncthreads();  // LDS is reused by the next piece
 }
 
+// The work of one cache block, bf16, with its K and V tiles in LDS at kt / vt
+// (the pool's own layouts): S^T = K Q^T on the matrix cores, mask and logit
+// transform, online softmax with lazy rescale, O^T += V^T P^T.  `newtok`: the
+// block holds the fused append's new token (its rows are substituted and
+// written to the pool).  The running state (o, m_run, l_run) is the caller's.
+template <int D, bool FUSE, bool EVICT>
+__device__ __forceinline__ void ring_block_step(const DecodeArgs& a, const LogitXform& xf,
+                                                const char* kt, const char* vt, bool ok, int tok0,
+                                                bool newtok, const NewToken<2, D>& nt,
+                                                const SeqSpan& sp, const SinkPart& sk, int b, int g,
+                                                const u32x4 (&qf)[D / 32], f32x4 (&o)[D / 16],
+                                                float& m_run, float& l_run) {
+  constexpr int KS = D / 32;  // score products
+  constexpr int XT = D / 16;  // output tiles
+  constexpr float kLazy = 8.0f;
+  const int lane = threadIdx.x & 63, c = lane & 15, j = lane >> 4;
+  const int G = a.gqa_group;
+  u32x4 kf[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const u32x4*>(kt + (64 * s + lane) * 16);
+  if constexpr (FUSE)
+    if (newtok) nt.put_k(kf, lane);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int s = 0; s < KS; ++s) acc = mma_bf16_k32(kf[s], qf[s], acc);
+  u32x2 vf[XT];
+#pragma unroll
+  for (int x = 0; x < XT; ++x)
+    vf[x] = *reinterpret_cast<const u32x2*>(vt + (16 * x + c) * 2 * kBlock + 8 * j);
+  if constexpr (FUSE) {
+    if (newtok) {
+      nt.put_v(vf, lane);
+      nt.store(lane);
+    }
+  }
+  mma_result_fence();
+
+  float s2[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = tok0 + 4 * j + r;
+    bool vis;
+    if constexpr (EVICT)
+      vis = ok & sk.visible(sp, t);
+    else
+      vis = ok & (t >= sp.vis_lo) & (t < sp.L);
+    s2[r] = vis ? xf(acc[r]) : kNegInf;
+  }
+  if constexpr (EVICT) put_scores(a, b, g * G + c, c < G, tok0 + 4 * j, s2);
+  float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
+  mx = quad_max(mx);
+  if (__any(mx > m_run + kLazy)) {
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+    l_run *= alpha;
+#pragma unroll
+    for (int x = 0; x < XT; ++x) o[x] *= alpha;
+    m_run = m_new;
+  }
+  const float m_use = m_run == kNegInf ? 0.f : m_run;
+  float p[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s2[r] - m_use);
+  l_run += (p[0] + p[1]) + (p[2] + p[3]);
+  const u32x2 pa = {pack_bf16x2_hw(p[0], p[1]), pack_bf16x2_hw(p[2], p[3])};
+  if (tok0 + kBlock > sp.L) {  // tokens past the context may hold anything
+    const int nv = sp.L - tok0, t0 = 4 * j;
+    const uint32_t mlo = (t0 + 0 < nv ? 0x0000FFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
+    const uint32_t mhi = (t0 + 2 < nv ? 0x0000FFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
+#pragma unroll
+    for (int x = 0; x < XT; ++x) vf[x] = u32x2{vf[x].x & mlo, vf[x].y & mhi};
+  }
+#pragma unroll
+  for (int x = 0; x < XT; ++x) o[x] = mma_bf16_k16(vf[x], pa, o[x]);
+}
+
 // LDS bytes of the ring each wave of the LDS form streams its blocks through,
 // and workgroups per CU: 32 KiB rings and one workgroup per CU at head_dim
 // 128 and 256 (four and two blocks in flight per wave); at head_dim 64 two
@@ -829,7 +905,6 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
 #pragma unroll
   for (int x = 0; x < XT; ++x) o[x] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
-  constexpr float kLazy = 8.0f;
 
   const int span = j1 - j0 - wave;
   const int nw = span > 0 ? (span + kWaves - 1) / kWaves : 0;
@@ -887,64 +962,9 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
     const int tok0 =
         (EVICT ? sk.blk(sp, j0 + wave + kWaves * i) : sp.first_blk + j0 + wave + kWaves * i) * kBlock;
 
-    u32x4 kf[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const u32x4*>(kt + (64 * s + lane) * 16);
     const bool newtok = FUSE && nt.own && i == nw - 1;
-    if constexpr (FUSE)
-      if (newtok) nt.put_k(kf, lane);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) acc = mma_bf16_k32(kf[s], qf[s], acc);
-    u32x2 vf[XT];
-#pragma unroll
-    for (int x = 0; x < XT; ++x)
-      vf[x] = *reinterpret_cast<const u32x2*>(vt + (16 * x + c) * 2 * kBlock + 8 * j);
-    if constexpr (FUSE) {
-      if (newtok) {
-        nt.put_v(vf, lane);
-        nt.store(lane);
-      }
-    }
-    mma_result_fence();
-
-    float s2[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = tok0 + 4 * j + r;
-      bool vis;
-      if constexpr (EVICT)
-        vis = ok & sk.visible(sp, t);
-      else
-        vis = ok & (t >= sp.vis_lo) & (t < sp.L);
-      s2[r] = vis ? xf(acc[r]) : kNegInf;
-    }
-    if constexpr (EVICT) put_scores(a, b, g * G + c, c < G, tok0 + 4 * j, s2);
-    float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-    mx = quad_max(mx);
-    if (__any(mx > m_run + kLazy)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
-      l_run *= alpha;
-#pragma unroll
-      for (int x = 0; x < XT; ++x) o[x] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s2[r] - m_use);
-    l_run += (p[0] + p[1]) + (p[2] + p[3]);
-    const u32x2 pa = {pack_bf16x2_hw(p[0], p[1]), pack_bf16x2_hw(p[2], p[3])};
-    if (tok0 + kBlock > sp.L) {  // tokens past the context may hold anything
-      const int nv = sp.L - tok0, t0 = 4 * j;
-      const uint32_t mlo = (t0 + 0 < nv ? 0x0000FFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
-      const uint32_t mhi = (t0 + 2 < nv ? 0x0000FFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
-#pragma unroll
-      for (int x = 0; x < XT; ++x) vf[x] = u32x2{vf[x].x & mlo, vf[x].y & mhi};
-    }
-#pragma unroll
-    for (int x = 0; x < XT; ++x) o[x] = mma_bf16_k16(vf[x], pa, o[x]);
+    ring_block_step<D, FUSE, EVICT>(a, xf, kt, vt, ok, tok0, newtok, nt, sp, sk, b, g, qf, o, m_run,
+                                    l_run);
     asm volatile("" ::: "memory");
     issue(i + NS);  // into the slot just read (the products have their operands)
   }
@@ -1085,7 +1105,6 @@ __device__ void run_piece_stream(const DecodeArgs& a, const LogitXform& xf, cons
 #pragma unroll
   for (int x = 0; x < XT; ++x) o[x] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = kNegInf, l_run = 0.f;
-  constexpr float kLazy = 8.0f;
 
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
@@ -1148,59 +1167,9 @@ __device__ void run_piece_stream(const DecodeArgs& a, const LogitXform& xf, cons
     const char* vt = kt + kTileBytes;
     const int tok0 = (sp.first_blk + j0 + wave + kWaves * i) * kBlock;
 
-    u32x4 kf[KS];
-#pragma unroll
-    for (int s = 0; s < KS; ++s) kf[s] = *reinterpret_cast<const u32x4*>(kt + (64 * s + lane) * 16);
     const bool newtok = FUSE && nt.own && i == nw - 1;
-    if constexpr (FUSE)
-      if (newtok) nt.put_k(kf, lane);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) acc = mma_bf16_k32(kf[s], qf[s], acc);
-    u32x2 vf[XT];
-#pragma unroll
-    for (int x = 0; x < XT; ++x)
-      vf[x] = *reinterpret_cast<const u32x2*>(vt + (16 * x + c) * 2 * kBlock + 8 * j);
-    if constexpr (FUSE) {
-      if (newtok) {
-        nt.put_v(vf, lane);
-        nt.store(lane);
-      }
-    }
-    mma_result_fence();
-
-    float s2[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = tok0 + 4 * j + r;
-      const bool vis = ok & (t >= sp.vis_lo) & (t < sp.L);
-      s2[r] = vis ? xf(acc[r]) : kNegInf;
-    }
-    float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-    mx = quad_max(mx);
-    if (__any(mx > m_run + kLazy)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
-      l_run *= alpha;
-#pragma unroll
-      for (int x = 0; x < XT; ++x) o[x] *= alpha;
-      m_run = m_new;
-    }
-    const float m_use = m_run == kNegInf ? 0.f : m_run;
-    float p[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s2[r] - m_use);
-    l_run += (p[0] + p[1]) + (p[2] + p[3]);
-    const u32x2 pa = {pack_bf16x2_hw(p[0], p[1]), pack_bf16x2_hw(p[2], p[3])};
-    if (tok0 + kBlock > sp.L) {  // tokens past the context may hold anything
-      const int nv = sp.L - tok0, t0 = 4 * j;
-      const uint32_t mlo = (t0 + 0 < nv ? 0x0000FFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
-      const uint32_t mhi = (t0 + 2 < nv ? 0x0000FFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
-#pragma unroll
-      for (int x = 0; x < XT; ++x) vf[x] = u32x2{vf[x].x & mlo, vf[x].y & mhi};
-    }
-#pragma unroll
-    for (int x = 0; x < XT; ++x) o[x] = mma_bf16_k16(vf[x], pa, o[x]);
+    ring_block_step<D, FUSE, false>(a, xf, kt, vt, ok, tok0, newtok, nt, sp, SinkPart{0, 0}, b, g, qf,
+                                    o, m_run, l_run);
     asm volatile("" ::: "memory");
     issue(i + NS, false);  // into the slot just read (the products have their operands)
   }
