@@ -402,7 +402,7 @@ __device__ void combine_waves(const DecodeArgs& a, const Piece& pc, const float*
 // (base-2 logits s2, -inf where not visible), stored in natural-log units.
 __device__ __forceinline__ void put_scores(const DecodeArgs& a, int b, int h, bool row_ok, int tok,
                                            const float (&s2)[4]) {
-  if (!row_ok) return;
+  if (!row_ok || a.scores == nullptr) return;  // sink tokens without logits: nothing to store
   const int Hq = a.num_kv_heads * a.gqa_group;
   float* dst = a.scores + ((size_t)b * Hq + h) * a.score_stride + tok;
   *reinterpret_cast<f32x4*>(dst) = f32x4{s2[0] * kLn2, s2[1] * kLn2, s2[2] * kLn2, s2[3] * kLn2};
@@ -1594,7 +1594,7 @@ hipError_t launch_d(DecodeArgs a, hipStream_t stream) {
     return a.k_new ? launch_k(decode_kernel<BF16, D, true, true, false>, a, lds, stream)
                    : launch_k(decode_kernel<BF16, D, true, false, false>, a, lds, stream);
   }
-  if (a.scores) {  // balanced split with per-head logits, then the column mass
+  if (a.scores || a.sink > 0) {  // sink tokens and/or per-head logits (then the column mass)
     hipError_t e = launch_k(decode_kernel<BF16, D, false, false, true>, a, lds, stream);
     if (e != hipSuccess || a.column_mass == nullptr) return e;
     const dim3 grid((a.score_stride + kThreads - 1) / kThreads, a.num_seqs * a.num_kv_heads);

@@ -85,6 +85,32 @@ def test_sink_decode_and_column_mass(spec):
     check_mass(mass, case, S, "column mass")
 
 
+@pytest.mark.parametrize("spec", SPECS, ids=lambda s: f"L{len(s[0])}-G{s[1]//s[2]}-D{s[3]}-{s[4]}-w{s[6]}-s{s[7]}")
+def test_sink_decode_without_mass(spec):
+    """AttentionSink alone (no logits, no column mass): the sink tokens stay
+    visible beside the window all the same."""
+    lens, Hq, Hkv, D, dtype, cap, W, S = spec
+    case = wl.make_decode_case(820 + D + S, lens, Hq, Hkv, D, dtype, softcap=cap, window=W)
+    banner("sink decode, no mass", spec)
+    out, lse, _ = run(case, S, with_mass=False)
+    ref, ref_lse = oracle.decode(case.q, case.k_pool, case.v_pool, case.block_tables,
+                                 case.context_lens, case.scale, case.softcap, case.window, dtype,
+                                 sink=S)
+    check_close(out, ref, dtype, "sink decode, no mass")
+    check_lse(lse, ref_lse, "sink decode, no mass")
+
+
+def test_sliding_window_workload_with_sinks_no_mass_full():
+    case = wl.sliding_window_decode()
+    banner(case.name, "sink 4, no mass")
+    out, lse, _ = run(case, 4, with_mass=False)
+    ref, ref_lse = oracle.decode(case.q, case.k_pool, case.v_pool, case.block_tables,
+                                 case.context_lens, case.scale, case.softcap, case.window,
+                                 case.dtype, sink=4)
+    check_close(out, ref, case.dtype, case.name)
+    check_lse(lse, ref_lse, case.name)
+
+
 def test_sink_decode_without_mass_equals_plain_decode_when_sink_is_zero():
     case = wl.make_decode_case(830, [3000, 17, 900, 2048], 8, 2, 256, "bf16", softcap=50.0,
                                window=512)
