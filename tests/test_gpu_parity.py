@@ -78,6 +78,8 @@ SMALL_DECODE = [
     ([2000, 12, 700], 16, 1, 256, "bf16", 30.0, 0),    # group 16
     ([40, 17], 2, 1, 128, "f32", 1.5, 16),
     ([4096] * 3 + [17], 8, 2, 256, "bf16", 50.0, 512),
+    ([5, 70, 300, 1000], 8, 2, 256, "f32", 10.0, 0),   # fp32 at head_dim 256
+    ([700, 33, 1], 16, 1, 256, "f32", 0.0, 100),       # fp32, group 16, window
 ]
 
 
