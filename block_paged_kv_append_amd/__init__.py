@@ -61,8 +61,15 @@ SIGNATURES = {
     "pkv_decode_graph_destroy": (None, [_P]),
     "paged_attn_mixed": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I,
                                         _I, _I, _I, _I, _F, _F, _I, _P, _Z, _I, _P]),
+    "pkv_check_paged_metadata": (ctypes.c_int, [_P, _P, _I, _I, _I, _P, _I, _P, _P]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
+
+# flag bits of pkv_check_paged_metadata
+CHECK_BAD_CONTEXT_LEN = 1
+CHECK_BAD_BLOCK_ID = 2
+CHECK_BAD_SLOT = 4
+CHECK_DUPLICATE_SLOT = 8
 
 
 class PkvError(RuntimeError):
@@ -187,6 +194,35 @@ def paged_kv_copy_blocks(src_ids, dst_ids, k_pool, v_pool, stream=None) -> None:
                                   _i32(src_ids, "src_ids"), _i32(dst_ids, "dst_ids"), n,
                                   _dtype_code(k_pool), _stream(stream))
     _check("paged_kv_copy_blocks", rc)
+
+
+def check_paged_metadata(num_blocks, block_tables=None, context_lens=None, slot_mapping=None,
+                         stream=None) -> int:
+    """Check block tables / context lengths ([B, MB] / [B] int32 device tensors)
+    and an append's slot mapping ([T] int32) against a pool of ``num_blocks``
+    blocks on the device; returns the OR of the CHECK_* flags (0: all valid).
+    Waits for the stream to reach the check."""
+    import torch
+
+    B = 0 if block_tables is None else block_tables.shape[0]
+    MB = 1 if block_tables is None else block_tables.shape[1]
+    if B and (context_lens is None or context_lens.numel() != B):
+        raise ValueError("context_lens must have one entry per block-table row")
+    T = 0 if slot_mapping is None else slot_mapping.numel()
+    src = block_tables if block_tables is not None else slot_mapping
+    dev = src.device if src is not None else torch.device("cuda")
+    flags = torch.empty(1, dtype=torch.int32, device=dev)
+    lib = load_library()
+    rc = lib.pkv_check_paged_metadata(
+        _i32(block_tables, "block_tables") if B else None,
+        _i32(context_lens, "context_lens") if B else None, B, MB, int(num_blocks),
+        _i32(slot_mapping, "slot_mapping") if T else None, T, _ptr(flags), _stream(stream))
+    _check("pkv_check_paged_metadata", rc)
+    if stream is None:
+        torch.cuda.current_stream(dev).synchronize()
+    else:
+        stream.synchronize()
+    return int(flags.item()) & 0xFFFFFFFF
 
 
 class BlockAllocator:

@@ -291,6 +291,30 @@ int paged_kv_copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks, int32_t
   return from_hip(pkv::launch_copy_blocks(a, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+int pkv_check_paged_metadata(const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                             const int32_t* slot_mapping, int32_t num_slots, uint32_t* flags,
+                             struct ihipStream_t* stream) {
+  const char* fn = "pkv_check_paged_metadata";
+  if (num_seqs < 0 || num_slots < 0)
+    return fail(PKV_EINVAL, "%s: num_seqs %d, num_slots %d", fn, num_seqs, num_slots);
+  if (max_blocks_per_seq < 1 || num_blocks < 1)
+    return fail(PKV_EINVAL, "%s: max_blocks_per_seq %d, num_blocks %d", fn, max_blocks_per_seq,
+                num_blocks);
+  if ((long long)num_blocks * PKV_BLOCK_SIZE > INT_MAX)
+    return fail(PKV_EINVAL, "%s: %d blocks overflow the int32 slot range", fn, num_blocks);
+  if (flags == nullptr) return fail(PKV_EINVAL, "%s: null flags", fn);
+  if (num_seqs > 0 && (block_tables == nullptr || context_lens == nullptr))
+    return fail(PKV_EINVAL, "%s: null block_tables or context_lens", fn);
+  if (num_slots > 0 && slot_mapping == nullptr) return fail(PKV_EINVAL, "%s: null slot_mapping", fn);
+  if (!aligned(flags, 4) || !aligned(block_tables, 4) || !aligned(context_lens, 4) ||
+      !aligned(slot_mapping, 4))
+    return fail(PKV_EINVAL, "%s: misaligned pointer", fn);
+  pkv::CheckArgs a{block_tables, context_lens, slot_mapping, num_seqs, max_blocks_per_seq,
+                   num_blocks, num_slots, flags};
+  return from_hip(pkv::launch_check(a, reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 size_t paged_attn_decode_workspace_size(int32_t num_seqs, int32_t num_kv_heads,
                                         int32_t gqa_group, int32_t head_dim,
                                         int32_t max_context_len, int32_t partition_size) {

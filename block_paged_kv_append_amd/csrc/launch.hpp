@@ -105,7 +105,25 @@ size_t decode_num_slots(int32_t num_seqs, int32_t num_kv_heads, int32_t max_cont
 size_t decode_workspace_bytes(int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
                               int32_t head_dim, int32_t max_context_len, int32_t partition_size);
 
+// Check of the caller's metadata (pkv_check_paged_metadata): flag bits.
+constexpr uint32_t kCheckBadContextLen = 1u;   // a length < 0 or > max_blocks_per_seq * 16
+constexpr uint32_t kCheckBadBlockId = 2u;      // a table entry the sequence reads is outside the pool
+constexpr uint32_t kCheckBadSlot = 4u;         // a slot >= num_blocks * 16
+constexpr uint32_t kCheckDuplicateSlot = 8u;   // two rows share a non-negative slot
+
+struct CheckArgs {
+  const int32_t* block_tables;  // may be null when num_seqs == 0
+  const int32_t* context_lens;
+  const int32_t* slot_mapping;  // may be null when num_slots == 0
+  int32_t num_seqs;
+  int32_t max_blocks_per_seq;
+  int32_t num_blocks;
+  int32_t num_slots;
+  uint32_t* flags;  // one word, cleared, then ORed
+};
+
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, bool bf16, hipStream_t stream);

@@ -119,6 +119,38 @@ int paged_kv_copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks, int32_t
                          struct ihipStream_t* stream);
 
 /*
+ * pkv_check_paged_metadata -- check, on the device, the caller's side of the
+ * contract every other entry point trusts: the block tables and context
+ * lengths (page "Inference Server", section "The engine": K/V in fixed-size
+ * blocks reached through per-sequence block tables) and an append's slot
+ * mapping.  The attention and append kernels never read or write outside
+ * the pools when these arrays are wrong, but their results are then
+ * unspecified; this call reports the mistake instead.
+ *
+ *   block_tables  int32 [num_seqs, max_blocks_per_seq]   (null if num_seqs == 0)
+ *   context_lens  int32 [num_seqs]                       (null if num_seqs == 0)
+ *   slot_mapping  int32 [num_slots]                      (null if num_slots == 0)
+ *   flags         uint32 [1] device word: cleared, then the OR of
+ *     PKV_CHECK_BAD_CONTEXT_LEN  some context_lens[b] < 0 or > max_blocks_per_seq * 16
+ *     PKV_CHECK_BAD_BLOCK_ID     some entry block_tables[b][j] with j * 16 < context_lens[b]
+ *                                (an entry the sequence reads) outside [0, num_blocks)
+ *     PKV_CHECK_BAD_SLOT         some slot >= num_blocks * 16 (negative slots are skips)
+ *     PKV_CHECK_DUPLICATE_SLOT   two rows share a non-negative slot
+ * Entries past a sequence's length are not checked.  The word is valid once
+ * the stream reaches the call.  The duplicate test compares every pair of
+ * slots (num_slots^2 reads): a debugging aid, not for the serving loop.
+ * Calls sharing one flags word must not overlap in time.
+ */
+#define PKV_CHECK_BAD_CONTEXT_LEN 1u
+#define PKV_CHECK_BAD_BLOCK_ID 2u
+#define PKV_CHECK_BAD_SLOT 4u
+#define PKV_CHECK_DUPLICATE_SLOT 8u
+int pkv_check_paged_metadata(const int32_t* block_tables, const int32_t* context_lens,
+                             int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
+                             const int32_t* slot_mapping, int32_t num_slots, uint32_t* flags,
+                             struct ihipStream_t* stream);
+
+/*
  * pkv_block_allocator -- the host side of refcounted blocks (page "Inference
  * Server", section "The engine"): hands out block ids, counts the block
  * tables holding each block, and prepares copy-on-write before a sequence

@@ -157,3 +157,25 @@ def test_prefill_rejects_bad_arguments():
     assert call(mq=65) == -1      # longer than any context
     assert call(cu=None) == -1
     assert call(Tq=-1) == -1
+
+
+def test_metadata_check_rejects_bad_arguments():
+    lib = pkv.load_library()
+    ok = dict(bt=16, cl=16, B=2, MB=4, nb=8, sm=16, T=3, fl=16)
+
+    def call(**o):
+        a = dict(ok, **o)
+        return lib.pkv_check_paged_metadata(a["bt"], a["cl"], a["B"], a["MB"], a["nb"], a["sm"],
+                                            a["T"], a["fl"], None)
+
+    assert call(B=-1) == -1
+    assert call(T=-1) == -1
+    assert call(MB=0) == -1
+    assert call(nb=0) == -1
+    assert call(nb=2 ** 28) == -1   # slots would overflow int32
+    assert call(fl=None) == -1
+    assert call(bt=None) == -1
+    assert call(cl=None) == -1
+    assert call(sm=None) == -1
+    assert call(fl=18) == -1        # misaligned flags word
+    assert "pkv_check_paged_metadata" in pkv.pkv_last_error()

@@ -1,0 +1,114 @@
+"""pkv_check_paged_metadata on the device: valid metadata of the bench
+workloads reports nothing; each planted breach of the contract (a length out
+of range, a block id out of the pool in an entry the sequence reads, a slot
+out of the pool, a repeated slot) reports its own flag and only that; entries
+past a sequence's length are not checked.  The expected flags come from the
+contract restated in numpy below."""
+import numpy as np
+import pytest
+import torch
+
+import block_paged_kv_append_amd as pkv
+from block_paged_kv_append_amd import workloads as wl
+from tests.gpu_common import i32
+
+pytestmark = pytest.mark.gpu
+
+
+def expected_flags(block_tables, context_lens, num_blocks, slot_mapping):
+    bt = np.asarray(block_tables, dtype=np.int64).reshape(len(context_lens), -1)
+    span = bt.shape[1] * 16
+    f = 0
+    for b, L in enumerate(np.asarray(context_lens, dtype=np.int64)):
+        if L < 0 or L > span:
+            f |= pkv.CHECK_BAD_CONTEXT_LEN
+        Lc = min(max(L, 0), span)
+        read = bt[b, :(Lc + 15) // 16]
+        if ((read < 0) | (read >= num_blocks)).any():
+            f |= pkv.CHECK_BAD_BLOCK_ID
+    s = np.asarray(slot_mapping, dtype=np.int64)
+    s = s[s >= 0]
+    if (s >= num_blocks * 16).any():
+        f |= pkv.CHECK_BAD_SLOT
+    s = s[s < num_blocks * 16]
+    if len(np.unique(s)) != len(s):
+        f |= pkv.CHECK_DUPLICATE_SLOT
+    return f
+
+
+def run(bt, cl, nb, sm):
+    got = pkv.check_paged_metadata(nb, i32(bt) if bt is not None else None,
+                                   i32(cl) if cl is not None else None,
+                                   i32(sm) if sm is not None else None)
+    return got
+
+
+def test_bench_workloads_are_valid():
+    for c in (wl.gemma_decode(), wl.sliding_window_decode()):
+        print("case:", c.name, flush=True)
+        assert run(c.block_tables, c.context_lens, c.num_blocks, None) == 0
+    p = wl.chunked_prefill_shared_prefix()
+    print("case:", p.name, flush=True)
+    assert run(p.block_tables, p.context_lens, p.num_blocks, p.slot_mapping) == 0
+
+
+def test_each_breach_sets_its_flag():
+    rng = np.random.default_rng(5)
+    B, MB, NB = 6, 9, 40
+    bt = rng.integers(0, NB, size=(B, MB)).astype(np.int32)
+    cl = np.array([0, 1, 16, 17, 100, MB * 16], dtype=np.int32)
+    sm = rng.permutation(NB * 16)[:50].astype(np.int32)
+    sm[[3, 11]] = -1  # skipped rows
+    cases = {"valid": (bt, cl, sm)}
+    b2 = bt.copy(); b2[4, 6] = NB                     # entry 6 of a 100-token sequence is read
+    cases["block id past the pool"] = (b2, cl, sm)
+    b3 = bt.copy(); b3[3, 1] = -7                      # entry 1 of a 17-token sequence is read
+    cases["negative block id"] = (b3, cl, sm)
+    b4 = bt.copy(); b4[2, 1] = NB + 5; b4[0, :] = -1   # past the 16-token length / empty sequence
+    cases["entries past the length"] = (b4, cl, sm)
+    c5 = cl.copy(); c5[1] = MB * 16 + 1
+    cases["length past the table"] = (bt, c5, sm)
+    c6 = cl.copy(); c6[0] = -2
+    cases["negative length"] = (bt, c6, sm)
+    s7 = sm.copy(); s7[7] = NB * 16
+    cases["slot past the pool"] = (bt, cl, s7)
+    s8 = sm.copy(); s8[49] = s8[0]
+    cases["repeated slot"] = (bt, cl, s8)
+    s9 = sm.copy(); s9[:] = -1
+    cases["all rows skipped"] = (bt, cl, s9)
+    b10, c10, s10 = b2.copy(), c5.copy(), s8.copy(); s10[7] = NB * 16 + 3
+    cases["every breach"] = (b10, c10, s10)
+    seen = set()
+    for name, (b, c, s) in cases.items():
+        print("case:", name, flush=True)
+        want = expected_flags(b, c, NB, s)
+        assert run(b, c, NB, s) == want, name
+        seen.add(want)
+    assert {0, pkv.CHECK_BAD_BLOCK_ID, pkv.CHECK_BAD_CONTEXT_LEN, pkv.CHECK_BAD_SLOT,
+            pkv.CHECK_DUPLICATE_SLOT, 15} <= seen
+
+
+def test_large_slot_mapping_and_tables():
+    """Thousands of table entries and slots (many workgroups): one repeated
+    slot at the two ends, and one bad block id in the last entry of the last
+    sequence (read only if that sequence is long enough), are found."""
+    p = wl.chunked_prefill_shared_prefix()
+    sm = np.asarray(p.slot_mapping, dtype=np.int32).copy()
+    assert run(None, None, p.num_blocks, sm) == 0
+    sm[-1] = sm[0]
+    assert run(None, None, p.num_blocks, sm) == pkv.CHECK_DUPLICATE_SLOT
+    c = wl.gemma_decode()
+    bt = np.asarray(c.block_tables, dtype=np.int32).copy()
+    last = (int(c.context_lens[-1]) + 15) // 16 - 1  # the last entry the sequence reads
+    bt[-1, last] = c.num_blocks
+    want = expected_flags(bt, c.context_lens, c.num_blocks, [])
+    assert want == pkv.CHECK_BAD_BLOCK_ID
+    assert run(bt, c.context_lens, c.num_blocks, None) == want
+    bt[-1, last] = 0
+    bt[-1, last + 1:] = -1  # entries past the length are not checked
+    assert run(bt, c.context_lens, c.num_blocks, None) == 0
+
+
+def test_empty_check_reports_nothing():
+    assert pkv.check_paged_metadata(4) == 0
+    torch.cuda.synchronize()
