@@ -1,12 +1,15 @@
-"""Seeded random configurations through every decode form and the mixed
-batch, each compared with the float64 oracle.
+"""Seeded random configurations through every decode form, the chunked
+prefill (after its append) and the mixed batch, each compared with the
+float64 oracle.
 
 Each case draws a batch size, context lengths (empty sequences, single
 tokens and block boundaries included), head_dim, GQA group, an optional
 window and softcap, a query scale (flat or peaked softmax) and, for the
 split-K form, a partition size; the decode runs balanced, split-K, and as a
-fused tick (append of the newest token, then decode).  The mixed-batch cases
-draw chunk and decode-row counts.  The draws are fixed by the seeds below, so
+fused tick (append of the newest token, then decode).  The prefill cases draw
+cached and chunk lengths (empty prefixes, one-token chunks, block edges), a
+shared prefix, window, softcap, query scale and the pool dtype.  The
+mixed-batch cases draw chunk and decode-row counts.  The draws are fixed by the seeds below, so
 a failure names a reproducible case.
 """
 import numpy as np
@@ -17,12 +20,13 @@ import block_paged_kv_append_amd as pkv
 import oracle
 from block_paged_kv_append_amd import workloads as wl
 from tests.gpu_common import (as_f64, check_close, check_lse, dev, i32, oracle_decode, run_append,
-                              run_decode)
+                              run_decode, run_prefill)
 
 pytestmark = pytest.mark.gpu
 
 DECODE_SEEDS = list(range(900, 924))
 MIXED_SEEDS = list(range(950, 958))
+PREFILL_SEEDS = list(range(970, 986))
 
 
 def _banner(*what):
@@ -126,3 +130,41 @@ def test_random_mixed_batch(seed):
                                   case.context_lens, case.scale, case.softcap, case.window, "bf16")
     check_close(as_f64(out), ref, "bf16", f"mixed seed {seed}")
     check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, f"mixed seed {seed}")
+
+
+@pytest.mark.parametrize("seed", PREFILL_SEEDS)
+def test_random_prefill(seed):
+    """Append of the chunks' rows (pools bit-exact), then the chunked prefill
+    over prefix + chunk, element-wise against the oracle."""
+    rng = np.random.default_rng(seed)
+    dtype = "f32" if seed % 4 == 3 else "bf16"
+    D = int(rng.choice([64, 128, 256]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
+    Hkv = int(rng.choice([1, 2]))
+    B = int(rng.integers(1, 7))
+    shared = int(rng.choice([0, 0, 1, 2]))
+    cached = [int(x) for x in rng.integers(0, 700, size=B)]
+    kinds = rng.integers(0, 4, size=B)
+    cached = [0 if k == 0 else (16 * max(c // 16, 1) if k == 1 else c) for c, k in zip(cached, kinds)]
+    cached = [max(c, 16 * shared) for c in cached]
+    chunk = [int(x) for x in rng.integers(1, 300, size=B)]
+    chunk = [1 if k == 2 else c for c, k in zip(chunk, rng.integers(0, 5, size=B))]
+    window = int(rng.choice([0, 0, 33, 200]))
+    cap = float(rng.choice([0.0, 30.0]))
+    q_scale = float(rng.choice([1.0, 8.0]))
+    case = wl.make_prefill_case(seed, cached, chunk, G * Hkv, Hkv, D, dtype,
+                                shared_prefix_blocks=shared, softcap=cap, window=window,
+                                q_scale=q_scale)
+    _banner("random prefill", seed, dict(dtype=dtype, D=D, G=G, Hkv=Hkv, cached=cached,
+                                         chunk=chunk, shared=shared, window=window, cap=cap,
+                                         q_scale=q_scale))
+    kp, vp = run_append(case)
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           dtype)
+    assert np.array_equal(pkv.to_bits(kp), kr), f"seed {seed}: K pool differs"
+    assert np.array_equal(pkv.to_bits(vp), vr), f"seed {seed}: V pool differs"
+    out, lse = run_prefill(case, kp, vp)
+    ref, ref_lse = oracle.prefill(case.q, case.cu_q_lens, kr, vr, case.block_tables,
+                                  case.context_lens, case.scale, case.softcap, case.window, dtype)
+    check_close(out, ref, dtype, f"prefill seed {seed}")
+    check_lse(lse, ref_lse, f"prefill seed {seed}")
