@@ -107,6 +107,7 @@ def call_decode(**over):
     (dict(out=24), -1),               # not 16-byte aligned
     (dict(), -3),                     # no workspace
     (dict(workspace=256, workspace_bytes=16), -3),
+    (dict(num_seqs=16385, num_kv_heads=4, gqa_group=1), -2),  # 65540 > 65536 segments
 ])
 def test_decode_rejects_bad_arguments(over, code):
     assert call_decode(**over) == code

@@ -185,6 +185,23 @@ def test_decode_large_batch(B, mode, P):
     check_lse(lse, ref_lse, f"B={B} {mode}")
 
 
+@pytest.mark.gpu
+def test_decode_at_the_segment_limit():
+    """The largest batch one decode call takes: 16384 sequences x 4 kv heads
+    = 65536 (sequence, kv head) segments, each with its own merge counter;
+    contexts of 0-24 tokens (empty ones and single blocks among them), in the
+    balanced and the split-K form on one case."""
+    rng = np.random.default_rng(31)
+    lens = [int(x) for x in rng.integers(0, 25, size=16384)]
+    case = wl.make_decode_case(31, lens, 8, 4, 64, "bf16", softcap=20.0)
+    ref, ref_lse = oracle_decode(case)
+    for mode, P in (("balanced", None), ("splitk", 16)):
+        banner("decode at the segment limit", mode)
+        out, lse = run_decode(case, mode, P)
+        check_close(out, ref, "bf16", f"segment limit {mode}")
+        check_lse(lse, ref_lse, f"segment limit {mode}")
+
+
 # ---------------------------------------------------------------------------
 # the named workloads at full size
 # ---------------------------------------------------------------------------
