@@ -305,6 +305,24 @@ def test_chunked_prefill_full(q_scale):
     check_lse(lse, ref_lse, case.name)
 
 
+@pytest.mark.parametrize("window", [0, 700])
+def test_prefill_long_chunk(window):
+    """One 3000-token chunk on an empty cache (94 row tiles of one sequence,
+    causal across all of them) beside a one-row chunk after 1000 cached
+    tokens; append first, then prefill, against the oracle."""
+    case = wl.make_prefill_case(41, [0, 1000], [3000, 1], 8, 2, 128, "bf16", window=window)
+    banner("prefill long chunk", window)
+    kp, vp = run_append(case)
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           "bf16")
+    assert np.array_equal(pkv.to_bits(kp), kr) and np.array_equal(pkv.to_bits(vp), vr)
+    out, lse = run_prefill(case, kp, vp)
+    ref, ref_lse = oracle.prefill(case.q, case.cu_q_lens, kr, vr, case.block_tables,
+                                  case.context_lens, case.scale, case.softcap, case.window, "bf16")
+    check_close(out, ref, "bf16", f"long chunk window {window}")
+    check_lse(lse, ref_lse, f"long chunk window {window}")
+
+
 def test_prefill_single_row_equals_decode():
     """A one-token chunk is a decode step: both entry points agree."""
     case = wl.make_prefill_case(451, [100, 700, 31], [1, 1, 1], 8, 2, 256, "bf16", softcap=50.0)
