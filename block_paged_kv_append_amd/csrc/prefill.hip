@@ -280,6 +280,12 @@ __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk
   const int G = a.gqa_group, Hkv = a.num_kv_heads, Hq = G * Hkv;
   const int PPW = 32 / G;  // positions per wave
   const LogitXform xf = make_xform(a.scale, a.softcap);
+  // Scores are masked to -inf before the logit transform.  Without softcap
+  // that transform is one multiply, which must keep -inf: the factor is made
+  // positive by flipping the sign of q for a negative scale, and a zero scale
+  // becomes a tiny positive factor (-inf * 0 would be NaN).
+  const bool flip_q = !SC && xf.scale_log2 < 0.f;
+  const float pos_scale_log2 = fmaxf(fabsf(xf.scale_log2), 1e-30f);
 
   int item = blk;
   if (a.num_items % 8 == 0) item = (int)((unsigned)blk % 8u) * (a.num_items / 8) + (int)((unsigned)blk / 8u);
@@ -310,6 +316,11 @@ __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk
         reinterpret_cast<const uint16_t*>(a.q) + ((size_t)(r0 + min(pos, nq - 1)) * Hq + head) * D + 8 * kg;
 #pragma unroll
     for (int i = 0; i < KD; ++i) qf[i] = *reinterpret_cast<const u32x4*>(row + 16 * i);
+    if (flip_q) {
+      const uint32_t sgn = 0x80008000u;  // both bf16 halves of each word
+#pragma unroll
+      for (int i = 0; i < KD; ++i) qf[i] ^= u32x4{sgn, sgn, sgn, sgn};
+    }
     // the query fragments live in the accumulator file (the matrix cores
     // read operands from either file), leaving vector registers for operand
     // prefetch
@@ -446,7 +457,7 @@ __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk
       const float y = softcap_log2(x * xf.scale, xf.cap, xf.inv_cap);
       return x == kNegInf ? kNegInf : y;
     } else {
-      return x * xf.scale_log2;
+      return x * pos_scale_log2;
     }
   };
 

@@ -305,6 +305,25 @@ def test_chunked_prefill_full(q_scale):
     check_lse(lse, ref_lse, case.name)
 
 
+@pytest.mark.parametrize("scale", [-0.2, 0.0, 1e-3])
+@pytest.mark.parametrize("cap", [0.0, 20.0])
+def test_prefill_scale_sign(scale, cap):
+    """Negative, zero and tiny softmax scales, with and without softcap (the
+    matrix-core prefill folds the scale into its exponent when there is no
+    softcap): ragged chunks over cached prefixes, against the oracle."""
+    case = wl.make_prefill_case(43, [37, 0, 300], [70, 33, 1], 8, 2, 128, "bf16", scale=scale,
+                                softcap=cap, q_scale=4.0)
+    banner("prefill scale", scale, cap)
+    kp, vp = run_append(case)
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           "bf16")
+    out, lse = run_prefill(case, kp, vp)
+    ref, ref_lse = oracle.prefill(case.q, case.cu_q_lens, kr, vr, case.block_tables,
+                                  case.context_lens, case.scale, case.softcap, case.window, "bf16")
+    check_close(out, ref, "bf16", f"scale {scale} cap {cap}")
+    check_lse(lse, ref_lse, f"scale {scale} cap {cap}")
+
+
 @pytest.mark.parametrize("window", [0, 700])
 def test_prefill_long_chunk(window):
     """One 3000-token chunk on an empty cache (94 row tiles of one sequence,
