@@ -305,6 +305,22 @@ def test_chunked_prefill_full(q_scale):
     check_lse(lse, ref_lse, case.name)
 
 
+@pytest.mark.parametrize("scale", [-0.2, 0.0])
+@pytest.mark.parametrize("cap", [0.0, 20.0])
+def test_decode_scale_sign(scale, cap):
+    """Negative and zero softmax scales through the balanced, split-K and
+    fused-tick decode (with a window, so masked keys sit inside the walked
+    blocks), against the oracle."""
+    case = wl.make_decode_case(47, [0, 1, 40, 333, 17], 8, 2, 128, "bf16", scale=scale,
+                               softcap=cap, window=100, q_scale=4.0)
+    ref, ref_lse = oracle_decode(case)
+    for mode, P in (("balanced", None), ("splitk", 32)):
+        banner("decode scale", scale, cap, mode)
+        out, lse = run_decode(case, mode, P)
+        check_close(out, ref, "bf16", f"scale {scale} cap {cap} {mode}")
+        check_lse(lse, ref_lse, f"scale {scale} cap {cap} {mode}")
+
+
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 1e-3])
 @pytest.mark.parametrize("cap", [0.0, 20.0])
 def test_prefill_scale_sign(scale, cap):
