@@ -32,25 +32,14 @@
 // Inner loop per wave (bf16): S^T = K Q^T on the matrix cores with the GQA
 // group's query heads as the 16 columns (zero past the group), mask by
 // select, online softmax in base 2 with the row reductions across the four
-// lanes that share a head, then O^T += V^T P^T on the matrix cores.  Blocks
-// stream through registers (one block in flight per wave, two workgroups per
-// CU) or, at head_dim 256, through per-wave LDS rings filled by direct
-// buffer-to-LDS copies.
+// lanes that share a head, then O^T += V^T P^T on the matrix cores.  bf16
+// blocks stream through per-wave LDS rings filled by direct buffer-to-LDS
+// copies; fp32 blocks through registers.
 #include <algorithm>
 #include <type_traits>
 
 #include "attn_tile.hpp"
 #include "launch.hpp"
-
-// bf16: blocks streamed through per-wave LDS rings at every head_dim.  The
-// register form (blocks loaded into registers, two workgroups per CU) is kept
-// switched off: runs of its head_dim 64 / 128 instantiations gave wrong
-// results and memory faults whose cause was not found.
-#ifndef PKV_DECODE_REGISTER_FORM
-#define PKV_DECODE_REGISTER_FORM 0
-#endif
-template <int D>
-constexpr bool kRingForm = !PKV_DECODE_REGISTER_FORM;
 
 namespace pkv {
 namespace {
@@ -111,7 +100,9 @@ struct NewToken {
     own = j1 == sp.nb && nw > 0 && j0 + wave + kWaves * (nw - 1) == last;
     if (!own) return;
     const int phys = a.block_tables[(size_t)b * a.max_blocks_per_seq + sp.first_blk + last];
-    if ((unsigned)phys >= (unsigned)a.num_blocks) {  // an unreadable block: nothing to write
+    // an unreadable block, or a length beyond max_context_len (its clamped
+    // last position holds an older token): nothing to write
+    if ((unsigned)phys >= (unsigned)a.num_blocks || a.context_lens[b] > a.max_context_len) {
       own = false;
       return;
     }
@@ -589,182 +580,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_range(const void* base, i
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, kRawBufferWord3);
 }
 
-// One piece, bf16: every wave walks its own blocks (j0 + wave + 4 i) with its
-// own online softmax; the four waves are combined through LDS at the end.
-// Per block, on the matrix cores:
-//   S^T[16 tokens][16] = K Q^T   (D/32 products; columns = the group's G
-//                                 query heads, zero past G)
-//   O^T[D][16]        += V^T P^T (D/16 products)
-// O^T keeps a head's statistics in the lanes holding its scores, so the
-// softmax needs no exchange beyond the two row reductions.  K and V of the
-// next block are loaded as soon as the current one has been read by the
-// products (about one block in flight per wave, eight waves per CU); the loads
-// are buffer loads with a per-block byte range, empty for a block that may not
-// be read, so they are unconditional.  The query fragments and the output
-// accumulators live in the accumulator file.
-template <int D, bool FUSE, bool EVICT>
-__device__ void run_piece_bf16(const DecodeArgs& a, const LogitXform& xf, const Piece& pc,
-                               float* lds) {
-  constexpr int KS = D / 32;  // score products
-  constexpr int XT = D / 16;  // output tiles
-  constexpr int kTileBytes = D * kBlock * 2;
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int c = lane & 15, j = lane >> 4;
-  const int G = a.gqa_group, Hkv = a.num_kv_heads, Hq = G * Hkv;
-  // the piece is the same for every lane: keep it scalar, so that the load
-  // descriptors built from it are scalar too
-  const int b = __builtin_amdgcn_readfirstlane(pc.b), g = __builtin_amdgcn_readfirstlane(pc.g);
-  const int j0 = __builtin_amdgcn_readfirstlane(pc.j0), j1 = __builtin_amdgcn_readfirstlane(pc.j1);
-  SeqSpan sp;
-  sp.first_blk = __builtin_amdgcn_readfirstlane(pc.sp.first_blk);
-  sp.nb = __builtin_amdgcn_readfirstlane(pc.sp.nb);
-  sp.vis_lo = __builtin_amdgcn_readfirstlane(pc.sp.vis_lo);
-  sp.L = __builtin_amdgcn_readfirstlane(pc.sp.L);
-  const SinkPart sk = EVICT ? sink_part(sp, a.window, a.sink) : SinkPart{0, 0};
-
-  u32x4 qf[KS];
-  {
-    const uint16_t* qrow =
-        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * Hq + g * G + min(c, G - 1)) * D + 8 * j;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qf[s] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) asm volatile("" : "=a"(qf[s]) : "0"(qf[s]));
-  }
-
-  f32x4 o[XT];
-#pragma unroll
-  for (int x = 0; x < XT; ++x) o[x] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = kNegInf, l_run = 0.f;
-  constexpr float kLazy = 8.0f;  // rescale only when a head's max grows by 2^8
-
-  const int span = j1 - j0 - wave;
-  const int nw = span > 0 ? (span + kWaves - 1) / kWaves : 0;
-  const int* bt = EVICT ? a.block_tables + (size_t)b * a.max_blocks_per_seq
-                       : a.block_tables + (size_t)b * a.max_blocks_per_seq + sp.first_blk + j0 + wave;
-  // table entry of this wave's block idx
-  auto tbl_at = [&](int idx) { return EVICT ? bt[sk.blk(sp, j0 + wave + kWaves * idx)] : bt[kWaves * idx]; };
-  const char* kpool = reinterpret_cast<const char*>(a.k_pool);
-  const char* vpool = reinterpret_cast<const char*>(a.v_pool);
-  NewToken<2, D> nt;
-  if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
-  // this wave's table entries, 64 at a time (lane l: block tbase + l)
-  int tbase = 0;
-  int tbl = lane < nw ? tbl_at(lane) : 0;
-  auto ranges = [&](int i, bool& ok, __amdgpu_buffer_rsrc_t& rk, __amdgpu_buffer_rsrc_t& rv) {
-    if (i - tbase >= 64) {  // uniform, every 64 blocks
-      tbase += 64;
-      tbl = tbase + lane < nw ? tbl_at(tbase + lane) : 0;
-    }
-    const int phys = __builtin_amdgcn_readlane(tbl, (i - tbase) & 63);
-    ok = i < nw && (unsigned)phys < (unsigned)a.num_blocks;
-    const size_t off = ((size_t)(ok ? phys : 0) * Hkv + g) * kTileBytes;
-    rk = tile_range(kpool + off, ok ? kTileBytes : 0);
-    rv = tile_range(vpool + off, ok ? kTileBytes : 0);
-  };
-  // K fragment s: lane (token c, j) <- K[token c][dims 32 s + 8 j .. + 7]
-  // V fragment x: lane (dim c, j)  <- V[tokens 4 j .. 4 j + 3][dim 16 x + c]
-  u32x4 kb[KS];
-  u32x2 vb[XT];
-  auto load_k = [&](__amdgpu_buffer_rsrc_t r) {
-#pragma unroll
-    for (int s = 0; s < KS; ++s) kb[s] = __builtin_amdgcn_raw_buffer_load_b128(r, (64 * s + lane) * 16, 0, 0);
-  };
-  auto load_v = [&](__amdgpu_buffer_rsrc_t r) {
-#pragma unroll
-    for (int x = 0; x < XT; ++x)
-      vb[x] = __builtin_amdgcn_raw_buffer_load_b64(r, (16 * x + c) * 2 * kBlock + 8 * j, 0, 0);
-  };
-
-  if (nw > 0) {
-    bool ok;
-    __amdgpu_buffer_rsrc_t rk, rv;
-    ranges(0, ok, rk, rv);
-    load_k(rk);
-    load_v(rv);
-    for (int i = 0; i < nw; ++i) {
-      const int tok0 =
-          (EVICT ? sk.blk(sp, j0 + wave + kWaves * i) : sp.first_blk + j0 + wave + kWaves * i) * kBlock;
-      if constexpr (FUSE) {
-        if (nt.own && i == nw - 1) {
-          nt.put_k(kb, lane);
-          nt.put_v(vb, lane);
-          nt.store(lane);
-        }
-      }
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int s = 0; s < KS; ++s) acc = mma_bf16_k32(kb[s], qf[s], acc);
-      bool ok_next;
-      __amdgpu_buffer_rsrc_t rk_next, rv_next;
-      ranges(i + 1, ok_next, rk_next, rv_next);  // past the last block: empty ranges
-      mma_result_fence();  // the products have read K (and their scores are ready)
-      load_k(rk_next);
-
-      float s2[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = tok0 + 4 * j + r;
-        bool vis;
-        if constexpr (EVICT)
-          vis = ok & sk.visible(sp, t);
-        else
-          vis = ok & (t >= sp.vis_lo) & (t < sp.L);
-        s2[r] = vis ? xf(acc[r]) : kNegInf;
-      }
-      if constexpr (EVICT) put_scores(a, b, g * G + c, c < G, tok0 + 4 * j, s2);
-      float mx = fmaxf(fmaxf(s2[0], s2[1]), fmaxf(s2[2], s2[3]));
-      mx = quad_max(mx);  // over the 16 tokens: lanes c, c + 16, c + 32, c + 48
-      if (__any(mx > m_run + kLazy)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
-        l_run *= alpha;
-#pragma unroll
-        for (int x = 0; x < XT; ++x) o[x] *= alpha;
-        m_run = m_new;
-      }
-      const float m_use = m_run == kNegInf ? 0.f : m_run;
-      float p[4];
-#pragma unroll
-      for (int r = 0; r < 4; ++r) p[r] = fast_exp2(s2[r] - m_use);
-      l_run += (p[0] + p[1]) + (p[2] + p[3]);
-      const u32x2 pa = {pack_bf16x2_hw(p[0], p[1]), pack_bf16x2_hw(p[2], p[3])};
-      if (tok0 + kBlock > sp.L) {  // tokens past the context may hold anything
-        const int nv = sp.L - tok0, t0 = 4 * j;
-        const uint32_t lo = (t0 + 0 < nv ? 0x0000FFFFu : 0u) | (t0 + 1 < nv ? 0xFFFF0000u : 0u);
-        const uint32_t hi = (t0 + 2 < nv ? 0x0000FFFFu : 0u) | (t0 + 3 < nv ? 0xFFFF0000u : 0u);
-#pragma unroll
-        for (int x = 0; x < XT; ++x) vb[x] = u32x2{vb[x].x & lo, vb[x].y & hi};
-      }
-#pragma unroll
-      for (int x = 0; x < XT; ++x) o[x] = mma_bf16_k16(vb[x], pa, o[x]);
-      mma_result_fence();  // the products have read V
-      load_v(rv_next);
-      ok = ok_next;
-    }
-  }
-
-  // ---- combine the four waves through LDS ----
-  mma_result_fence();
-  const float l_tot = quad_sum(l_run);
-  float* lo = lds;                    // [4][G][D]
-  float* lml = lds + kWaves * G * D;  // [4][G][2]
-  if (c < G) {
-#pragma unroll
-    for (int x = 0; x < XT; ++x)
-      *reinterpret_cast<f32x4*>(lo + ((size_t)wave * G + c) * D + 16 * x + 4 * j) = o[x];
-    if (j == 0) {
-      lml[(wave * G + c) * 2] = m_run;
-      lml[(wave * G + c) * 2 + 1] = l_tot;
-    }
-  }
-  __syncthreads();
-  combine_waves<true, D, EVICT>(a, pc, lo, lml);
-  __syncthreads();  // LDS is reused by the next piece
-}
-
 // The work of one cache block, bf16, with its K and V tiles in LDS at kt / vt
 // (the pool's own layouts): S^T = K Q^T on the matrix cores, mask and logit
 // transform, online softmax with lazy rescale, O^T += V^T P^T.  `newtok`: the
@@ -863,9 +678,9 @@ constexpr int kRingWgsPerCu = D >= 128 ? 1 : 2;
 template <int D>
 constexpr int kPieceCost = PKV_DECODE_PIECE_COST_BYTES / (2 * kBlock * D * 2);
 
-// One piece, bf16, blocks streamed through LDS.  As run_piece_bf16 (each wave
-// walks its own blocks, O^T on the matrix cores, waves combined at the end),
-// but K and V reach LDS by direct buffer-to-LDS copies into a ring private to
+// One piece, bf16, blocks streamed through LDS.  Each wave walks its own
+// blocks (j0 + wave + 4 i) with its own online softmax, O^T on the matrix
+// cores, and the four waves are combined at the end.  K and V reach LDS by direct buffer-to-LDS copies into a ring private to
 // the wave: NS = 32 KiB / (16 KiB x D / 256) blocks in flight per wave, with no
 // vector registers held by loads and no barrier in the loop.  A block is
 // copied verbatim (its K tile, then its V tile, 1 KiB per copy), so the
@@ -1373,10 +1188,7 @@ template <bool BF16, int D, bool FIXED, bool FUSE, bool EVICT>
 __device__ __forceinline__ void decode_body(const DecodeArgs& a, int blk, float* lds) {
   auto run_one = [&](const LogitXform& xf, const Piece& pc) {
     if constexpr (BF16) {
-      if constexpr (kRingForm<D>)
-        run_piece_ring<D, FUSE, EVICT>(a, xf, pc, lds);
-      else
-        run_piece_bf16<D, FUSE, EVICT>(a, xf, pc, lds);
+      run_piece_ring<D, FUSE, EVICT>(a, xf, pc, lds);
     } else {
       run_piece<BF16, D, FUSE, EVICT>(a, xf, pc, lds);
     }
@@ -1513,7 +1325,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int blk, float*
 }
 
 template <bool BF16, int D, bool FIXED, bool FUSE, bool EVICT>
-__global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingForm<D> ? kRingWgsPerCu<D> : 2) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads, !BF16 ? 1 : kRingWgsPerCu<D>) void decode_kernel(DecodeArgs a) {
   extern __shared__ float lds[];
   decode_body<BF16, D, FIXED, FUSE, EVICT>(a, blockIdx.x, lds);
 }
@@ -1559,9 +1371,6 @@ hipError_t launch_k(K kernel, const DecodeArgs& a, size_t lds, hipStream_t strea
 #ifndef PKV_DECODE_WGS_PER_CU
 #define PKV_DECODE_WGS_PER_CU 1
 #endif
-#ifndef PKV_DECODE_BF16_WGS_PER_CU
-#define PKV_DECODE_BF16_WGS_PER_CU 2
-#endif
 #ifndef PKV_DECODE_MIN_BLOCKS_PER_WG
 #define PKV_DECODE_MIN_BLOCKS_PER_WG 8
 #endif
@@ -1571,16 +1380,15 @@ hipError_t launch_d(DecodeArgs a, hipStream_t stream) {
   if (a.part_blocks == 0) {
     long long n = (a.units_bound + PKV_DECODE_MIN_BLOCKS_PER_WG - 1) / PKV_DECODE_MIN_BLOCKS_PER_WG;
     const long long cap =
-        (long long)a.cu_count * (!BF16 ? PKV_DECODE_WGS_PER_CU
-                                       : kRingForm<D> ? kRingWgsPerCu<D> : PKV_DECODE_BF16_WGS_PER_CU);
+        (long long)a.cu_count * (!BF16 ? PKV_DECODE_WGS_PER_CU : kRingWgsPerCu<D>);
     n = min(n, min(cap, (long long)kMaxWorkers));
     a.num_workers = (int32_t)max(n, 1LL);
   }
   size_t lds = (size_t)kWaves * a.gqa_group * (D + 2) * sizeof(float);  // the waves' combine
   lds = std::max(lds, (size_t)(4 * kThreads + 2 * 16) * sizeof(float));  // a merge
-  if (BF16 && kRingForm<D>) lds = std::max(lds, (size_t)kWaves * kRingBytesPerWave<D>);
+  if (BF16) lds = std::max(lds, (size_t)kWaves * kRingBytesPerWave<D>);
   if (a.part_blocks > 0) {
-    if constexpr (BF16 && kRingForm<D>) {
+    if constexpr (BF16) {
       if (PKV_DECODE_FIXED_STREAM && fixed_stream_lds<D>(a.gqa_group) <= kLdsPerCu) {
         // persistent form: one workgroup per CU, at most one per item
         DecodeArgs p = a;

@@ -76,7 +76,20 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
   const int p_hi = min(n - 1, pos_wave + RT * PP - 1);
   const int last_tok = min(shift + p_hi, L - 1);
   const int first_tok = a.window > 0 ? max(0, shift + pos_wave - a.window + 1) : 0;
-  if (last_tok < 0) return;
+  if (last_tok < 0) {
+    // every row of this wave sits before the cache (a chunk longer than its
+    // context, a caller error): no key is visible, out = 0 and lse = -inf
+#pragma unroll
+    for (int t = 0; t < RT; ++t) {
+      const int pos = pos_wave + t * PP + c / G;
+      if (pos >= n) continue;
+      const size_t row = (size_t)(r0 + pos) * Hq + g * G + c % G;
+      if (a.lse != nullptr && j == 0) a.lse[row] = kNegInf;
+      T* dst = reinterpret_cast<T*>(a.out) + row * D;
+      for (int d = j; d < D; d += 4) store1(dst + d, 0.f);
+    }
+    return;
+  }
   const int blk_lo = first_tok / kBlock, blk_hi = last_tok / kBlock;
 
   f32x4 o[RT][NT];
@@ -331,7 +344,18 @@ __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk
   // keys the workgroup's rows can see
   const int p_hi = min(nq - 1, pos_wg + kWaves * PPW - 1);
   const int last_tok = min(shift + p_hi, L - 1);
-  if (last_tok < 0) return;
+  if (last_tok < 0) {
+    // every row of the workgroup sits before the cache (a chunk longer than
+    // its context, a caller error): no key is visible, out = 0, lse = -inf
+    if (wave_live && rvalid) {
+      const size_t row = (size_t)(r0 + pos) * Hq + head;
+      if (a.lse != nullptr && kg == 0) a.lse[row] = kNegInf;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + row * D + 4 * kg;
+#pragma unroll
+      for (int x = 0; x < D / 8; ++x) *reinterpret_cast<u32x2*>(dst + 8 * x) = u32x2{0u, 0u};
+    }
+    return;
+  }
   const int first_tok = a.window > 0 ? max(0, shift + pos_wg - a.window + 1) : 0;
   const int blk_lo = first_tok / kBlock;
   const int nblk = last_tok / kBlock - blk_lo + 1;

@@ -279,8 +279,10 @@ int paged_attn_decode_splitk(void* out, float* lse, const void* q, const void* k
  * goes to slot block_tables[b][(L_b - 1) / 16] * 16 + (L_b - 1) % 16 of every
  * kv head, exactly as paged_kv_append with those slots would write it, and
  * the outputs equal those of paged_kv_append followed by paged_attn_decode
- * (or _splitk).  Sequences with L_b == 0, or whose entry for that block is
- * outside [0, num_blocks), append nothing.  Within one call, no block that
+ * (or _splitk).  Sequences with L_b == 0, with context_lens[b] >
+ * max_context_len (a caller error: the clamped position holds an older
+ * token, which is left alone), or whose entry for that block is outside
+ * [0, num_blocks), append nothing.  Within one call, no block that
  * receives a token may be read by another sequence (a block shared by
  * several sequences is copied before it is appended to).
  * Errors as paged_attn_decode; PKV_EINVAL also for a missing or misaligned
@@ -379,6 +381,8 @@ void pkv_decode_graph_destroy(pkv_decode_graph* graph);
  *   max_q_len     >= every n_b = cu_q_lens[b+1] - cu_q_lens[b]
  *   context_lens  int32 [num_seqs], L_b >= n_b; query row j of sequence b
  *                 sits at position L_b - n_b + j and sees keys t <= position
+ *                 (rows at negative positions, L_b < n_b, a caller error,
+ *                 see no key: out = 0 and lse = -inf)
  *   gqa_group     1, 2, 4, 8 or 16
  */
 int paged_attn_prefill(void* out, float* lse, const void* q, const int32_t* cu_q_lens,

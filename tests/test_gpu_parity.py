@@ -308,17 +308,83 @@ def test_chunked_prefill_full(q_scale):
 @pytest.mark.parametrize("scale", [-0.2, 0.0])
 @pytest.mark.parametrize("cap", [0.0, 20.0])
 def test_decode_scale_sign(scale, cap):
-    """Negative and zero softmax scales through the balanced, split-K and
-    fused-tick decode (with a window, so masked keys sit inside the walked
-    blocks), against the oracle."""
+    """Negative and zero softmax scales (with a window, so masked keys sit
+    inside the walked blocks) through every decode form, against the oracle:
+    the balanced and split-K decode, the fused tick (balanced and split-K),
+    the eviction-policy variant (sink tokens, logits and column mass) and the
+    decode rows of a one-launch mixed batch."""
     case = wl.make_decode_case(47, [0, 1, 40, 333, 17], 8, 2, 128, "bf16", scale=scale,
                                softcap=cap, window=100, q_scale=4.0)
+    what = f"scale {scale} cap {cap}"
     ref, ref_lse = oracle_decode(case)
     for mode, P in (("balanced", None), ("splitk", 32)):
         banner("decode scale", scale, cap, mode)
         out, lse = run_decode(case, mode, P)
-        check_close(out, ref, "bf16", f"scale {scale} cap {cap} {mode}")
-        check_lse(lse, ref_lse, f"scale {scale} cap {cap} {mode}")
+        check_close(out, ref, "bf16", f"{what} {mode}")
+        check_lse(lse, ref_lse, f"{what} {mode}")
+
+    # the fused tick: the newest rows appended and attended in one launch
+    kn, vn = wl.new_token_rows(case, 48)
+    tref, tref_lse, kr, vr = oracle.decode_append(case.q, kn, vn, case.k_pool, case.v_pool,
+                                                  case.block_tables, case.context_lens,
+                                                  case.scale, case.softcap, case.window, "bf16")
+    for P in (0, 32):
+        banner("decode scale tick", scale, cap, P)
+        q, kp, vp = dev(case.q, "bf16"), dev(case.k_pool, "bf16"), dev(case.v_pool, "bf16")
+        out = torch.empty_like(q)
+        lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+        pkv.paged_attn_decode_append(out, q, dev(kn, "bf16"), dev(vn, "bf16"), kp, vp,
+                                     i32(case.block_tables), i32(case.context_lens),
+                                     case.max_context_len, case.scale, case.softcap, case.window,
+                                     partition_size=P, lse=lse)
+        torch.cuda.synchronize()
+        assert np.array_equal(pkv.to_bits(kp), kr) and np.array_equal(pkv.to_bits(vp), vr)
+        check_close(as_f64(out), tref, "bf16", f"{what} tick P={P}")
+        check_lse(lse.cpu().numpy().astype(np.float64), tref_lse, f"{what} tick P={P}")
+
+    # the eviction-policy variant: 4 sink tokens beside the window, with logits and mass
+    banner("decode scale sink/h2o", scale, cap)
+    q, kp, vp = dev(case.q, "bf16"), dev(case.k_pool, "bf16"), dev(case.v_pool, "bf16")
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    S = -(-case.max_context_len // 16) * 16
+    scores = torch.full((case.num_seqs, case.num_q_heads, S), float("nan"), device="cuda")
+    mass = torch.full((case.num_seqs, case.num_kv_heads, S), float("nan"), device="cuda")
+    pkv.paged_attn_decode_sink_h2o(out, q, kp, vp, i32(case.block_tables), i32(case.context_lens),
+                                   case.max_context_len, case.scale, case.softcap, case.window, 4,
+                                   scores=scores, column_mass=mass, lse=lse)
+    torch.cuda.synchronize()
+    sref, sref_lse = oracle.decode(case.q, case.k_pool, case.v_pool, case.block_tables,
+                                   case.context_lens, case.scale, case.softcap, case.window, "bf16",
+                                   sink=4)
+    check_close(as_f64(out), sref, "bf16", f"{what} sink")
+    check_lse(lse.cpu().numpy().astype(np.float64), sref_lse, f"{what} sink")
+    mref = oracle.column_mass(case.q, case.k_pool, case.v_pool, case.block_tables,
+                              case.context_lens, case.scale, case.softcap, case.window, "bf16", 4,
+                              length=S)
+    got = mass.cpu().numpy().astype(np.float64)
+    assert not np.isnan(got).any() and np.all(np.abs(got - mref) <= 1e-5 + 5e-3 * np.abs(mref))
+
+    # a mixed batch: two chunks, then these sequences as decode rows
+    lens = case.context_lens.tolist()
+    m = wl.make_prefill_case(49, [60, 200] + [max(L - 1, 0) for L in lens],
+                             [70, 33] + [1] * len(lens), 8, 2, 128, "bf16",
+                             scale=scale, softcap=cap, window=100, q_scale=4.0)
+    banner("decode scale mixed", scale, cap)
+    kp, vp = run_append(m)
+    q = dev(m.q, "bf16")
+    out = torch.full_like(q, float("nan"))
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device="cuda")
+    cu = m.cu_q_lens[:3]
+    pkv.paged_attn_mixed(out, q, i32(cu), int(cu[-1]), 70, kp, vp, i32(m.block_tables),
+                         i32(m.context_lens), m.max_context_len, m.scale, m.softcap, m.window,
+                         lse=lse)
+    torch.cuda.synchronize()
+    kr, vr = oracle.append(m.k_new, m.v_new, m.slot_mapping, m.k_pool, m.v_pool, "bf16")
+    mref, mref_lse = oracle.prefill(m.q, m.cu_q_lens, kr, vr, m.block_tables, m.context_lens,
+                                    m.scale, m.softcap, m.window, "bf16")
+    check_close(as_f64(out), mref, "bf16", f"{what} mixed")
+    check_lse(lse.cpu().numpy().astype(np.float64), mref_lse, f"{what} mixed")
 
 
 @pytest.mark.parametrize("scale", [-0.2, 0.0, 1e-3])
