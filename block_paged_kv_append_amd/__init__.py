@@ -46,6 +46,8 @@ SIGNATURES = {
                                          _I, _F, _F, _I, _P, _Z, _I, _P]),
     "paged_attn_decode_splitk": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I,
                                                 _I, _I, _I, _F, _F, _I, _I, _P, _Z, _I, _P]),
+    "paged_attn_decode_no_alloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _I, _P, _I, _P, _I, _I, _I,
+                                                  _I, _I, _I, _F, _F, _I, _I, _I, _P]),
     "paged_attn_decode_append": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _P, _I,
                                                 _I, _I, _I, _I, _I, _F, _F, _I, _I, _P, _Z, _I,
                                                 _P]),
@@ -360,6 +362,23 @@ def paged_attn_decode_splitk(out, q, k_pool, v_pool, block_tables, context_lens,
                                       ws.numel() * ws.element_size(), _dtype_code(q),
                                       _stream(stream))
     _check("paged_attn_decode_splitk", rc)
+
+
+def paged_attn_decode_no_alloc(out, q, k_pool, v_pool, block_tables, context_lens,
+                               max_context_len, scale, softcap=0.0, window=0, partition_size=0,
+                               lse=None, stream=None) -> None:
+    """paged_attn_decode (partition_size 0) or paged_attn_decode_splitk
+    without a workspace: the library's static per-GPU scratch serves instead,
+    and nothing is allocated.  Calls that overlap on one GPU race."""
+    nb, hkv, d, B, G, MB = _decode_dims(out, q, k_pool, v_pool, block_tables, context_lens)
+    lib = load_library()
+    rc = lib.paged_attn_decode_no_alloc(_ptr(out), _ptr(lse), _ptr(q), _ptr(k_pool), _ptr(v_pool),
+                                        nb, _i32(block_tables, "block_tables"), MB,
+                                        _i32(context_lens, "context_lens"), int(max_context_len),
+                                        B, hkv, G, d, BLOCK_SIZE, float(scale), float(softcap),
+                                        int(window), int(partition_size), _dtype_code(q),
+                                        _stream(stream))
+    _check("paged_attn_decode_no_alloc", rc)
 
 
 def paged_attn_decode_append(out, q, k_new, v_new, k_pool, v_pool, block_tables, context_lens,

@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <mutex>
 
 #include "launch.hpp"
 
@@ -123,7 +124,8 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const Deco
                 int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group, int32_t head_dim,
                 int32_t block_size, float scale, float softcap, int32_t window,
                 int32_t partition_size, void* workspace, size_t workspace_bytes, int32_t dtype,
-                hipStream_t stream, pkv::DecodeArgs* build_only = nullptr) {
+                hipStream_t stream, pkv::DecodeArgs* build_only = nullptr,
+                bool check_only = false) {
   int rc = check_common(fn, out, lse, q, k_pool, v_pool, num_blocks, block_tables,
                         max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
                         gqa_group, head_dim, block_size, scale, softcap, dtype);
@@ -137,6 +139,7 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const Deco
   if ((long long)num_seqs * num_kv_heads > pkv::kMaxSegments)
     return fail(PKV_EUNSUPPORTED, "%s: num_seqs * num_kv_heads = %lld exceeds %d", fn,
                 (long long)num_seqs * num_kv_heads, pkv::kMaxSegments);
+  if (check_only) return PKV_OK;  // the arguments alone, before any workspace
   const size_t need = pkv::decode_workspace_bytes(num_seqs, num_kv_heads, gqa_group, head_dim,
                                                   max_context_len, partition_size);
   if (workspace == nullptr || workspace_bytes < need || !aligned(workspace, 256))
@@ -230,6 +233,58 @@ int record_error(int code, const char* fmt, ...) {
 }
 
 }  // namespace pkv
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free decode (paged_attn_decode_no_alloc): the
+// decode workspace (segment counters, then the partial results) as a static
+// device array, one copy per GPU, held until the process ends.  Its size is
+// the largest balanced-split workspace (group 16, head_dim 256): 32.5 MiB.
+// Host code never passes the array's name to a kernel (on the host it is a
+// stand-in, not a device address): the first call on each device looks up
+// the device address once and keeps it.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes =
+    pkv::kCounterBytes + ((2 * (size_t)pkv::kMaxWorkers * 16 * 256 * sizeof(float) + 255) & ~size_t(255)) +
+    ((2 * (size_t)pkv::kMaxWorkers * 16 * 2 * sizeof(float) + 255) & ~size_t(255));
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+__global__ void zero_words_kernel(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// The current device's scratch address; the first call on a device looks it
+// up and clears the counters (a kernel on `stream`, so that a call made
+// under graph capture records it instead of running it).
+int device_scratch(const char* fn, hipStream_t stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return from_hip(e, fn);
+  if (dev < 0 || dev >= kMaxDevices) return fail(PKV_EUNSUPPORTED, "%s: device %d", fn, dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return from_hip(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    const int words = (int)(pkv::kCounterBytes / sizeof(uint32_t));
+    zero_words_kernel<<<(words + 255) / 256, 256, 0, stream>>>(static_cast<uint32_t*>(p), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return from_hip(e, "clearing the scratch counters");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -357,6 +412,42 @@ int paged_attn_decode_splitk(void* out, float* lse, const void* q, const void* k
                      num_kv_heads, gqa_group, head_dim, block_size, scale, softcap, window,
                      partition_size, workspace, workspace_bytes, dtype,
                      reinterpret_cast<hipStream_t>(stream));
+}
+
+int paged_attn_decode_no_alloc(void* out, float* lse, const void* q, const void* k_pool,
+                               const void* v_pool, int32_t num_blocks,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t max_context_len,
+                               int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                               int32_t head_dim, int32_t block_size, float scale, float softcap,
+                               int32_t window, int32_t partition_size, int32_t dtype,
+                               struct ihipStream_t* stream) {
+  const char* fn = "paged_attn_decode_no_alloc";
+  if (partition_size < 0 || partition_size % PKV_BLOCK_SIZE != 0)
+    return fail(PKV_EUNSUPPORTED, "%s: partition_size %d is not 0 or a positive multiple of 16",
+                fn, partition_size);
+  // the same argument checks as the workspace form first, so that a bad call
+  // fails for its own reason before the scratch size is considered
+  int rc = decode_impl(fn, out, lse, q, DecodeExtras{}, k_pool, v_pool, num_blocks, block_tables,
+                       max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
+                       gqa_group, head_dim, block_size, scale, softcap, window, partition_size,
+                       nullptr, SIZE_MAX, dtype, reinterpret_cast<hipStream_t>(stream),
+                       nullptr, /*check_only=*/true);
+  if (rc != PKV_OK || num_seqs == 0) return rc;
+  const size_t need = pkv::decode_workspace_bytes(num_seqs, num_kv_heads, gqa_group, head_dim,
+                                                  max_context_len, partition_size);
+  if (need > kNoAllocScratchBytes)
+    return fail(PKV_EWORKSPACE,
+                "%s: these sizes need %zu bytes of scratch; the static scratch holds %zu (use "
+                "paged_attn_decode_splitk with a workspace, or a larger partition_size)",
+                fn, need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  rc = device_scratch(fn, reinterpret_cast<hipStream_t>(stream), &ws);
+  if (rc != PKV_OK) return rc;
+  return decode_impl(fn, out, lse, q, DecodeExtras{}, k_pool, v_pool, num_blocks, block_tables,
+                     max_blocks_per_seq, context_lens, max_context_len, num_seqs, num_kv_heads,
+                     gqa_group, head_dim, block_size, scale, softcap, window, partition_size, ws,
+                     kNoAllocScratchBytes, dtype, reinterpret_cast<hipStream_t>(stream));
 }
 
 int paged_attn_decode_append(void* out, float* lse, const void* q, const void* k_new,

@@ -261,6 +261,34 @@ int paged_attn_decode_splitk(void* out, float* lse, const void* q, const void* k
                              size_t workspace_bytes, int32_t dtype, struct ihipStream_t* stream);
 
 /*
+ * paged_attn_decode_no_alloc -- paged_attn_decode (partition_size == 0) or
+ * paged_attn_decode_splitk (partition_size > 0) without a caller workspace
+ * and without any allocation, for callers that cannot allocate device memory
+ * or pass a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments and results as those two
+ * entry points, minus the workspace.
+ *
+ * The workspace is a static device array of the library, 32.5 MiB per GPU
+ * (the largest balanced-split workspace: gqa_group 16, head_dim 256), held
+ * from the first call on a GPU until the process ends.  Sizes whose
+ * workspace would exceed it (paged_attn_decode_workspace_size) are rejected
+ * with PKV_EWORKSPACE; the balanced split (partition_size == 0) always fits.
+ * The first call on each GPU also enqueues, on `stream`, a small kernel that
+ * clears the array's counters; every completed call leaves them at zero.
+ * All calls on one GPU share the array: calls that overlap in time on one
+ * GPU (other streams, other threads, the first call included) race and give
+ * wrong results.  No hipMalloc, hipFree or other allocation is made.
+ */
+int paged_attn_decode_no_alloc(void* out, float* lse, const void* q, const void* k_pool,
+                               const void* v_pool, int32_t num_blocks,
+                               const int32_t* block_tables, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, int32_t max_context_len,
+                               int32_t num_seqs, int32_t num_kv_heads, int32_t gqa_group,
+                               int32_t head_dim, int32_t block_size, float scale, float softcap,
+                               int32_t window, int32_t partition_size, int32_t dtype,
+                               struct ihipStream_t* stream);
+
+/*
  * paged_attn_decode_append -- one decode tick in one launch: the append of
  * every sequence's newest token and the batched decode that attends to it.
  * Each tick appends the token every active request just produced and runs

@@ -180,3 +180,36 @@ def test_metadata_check_rejects_bad_arguments():
     assert call(sm=None) == -1
     assert call(fl=18) == -1        # misaligned flags word
     assert "pkv_check_paged_metadata" in pkv.pkv_last_error()
+
+
+def _no_alloc(lib, **over):
+    a = _decode_args(**over)
+    P = over.get("partition_size", 0)
+    return lib.paged_attn_decode_no_alloc(a["out"], a["lse"], a["q"], a["k_pool"], a["v_pool"],
+                                          a["num_blocks"], a["block_tables"],
+                                          a["max_blocks_per_seq"], a["context_lens"],
+                                          a["max_context_len"], a["num_seqs"], a["num_kv_heads"],
+                                          a["gqa_group"], a["head_dim"], a["block_size"],
+                                          a["scale"], a["softcap"], a["window"], P, a["dtype"],
+                                          a["stream"])
+
+
+def test_no_alloc_decode_rejects_on_the_host():
+    """The allocation-free decode checks its arguments like the workspace
+    forms, and rejects sizes whose workspace would not fit its static scratch,
+    all before any HIP call (no GPU here)."""
+    lib = pkv.load_library()
+    assert _no_alloc(lib, dtype=5) == -2
+    assert _no_alloc(lib, q=None) == -1
+    assert _no_alloc(lib, partition_size=24) == -2
+    assert _no_alloc(lib, num_seqs=0, out=None, q=None) == 0
+    # 64 x 8 segments of up to 8192 tokens in 16-token partitions, group 16 at
+    # head_dim 256: 2^18 partials of 16 KiB, far beyond the 32.5 MiB scratch
+    rc = _no_alloc(lib, num_seqs=64, num_kv_heads=8, gqa_group=16, head_dim=256,
+                   max_blocks_per_seq=512, max_context_len=8192, partition_size=16)
+    assert rc == -3
+    assert "static scratch" in pkv.pkv_last_error()
+    # the balanced split's largest workspace is exactly the scratch: accepted
+    # by the size check (it would launch here, so only the size is compared)
+    f = lib.paged_attn_decode_workspace_size
+    assert f(16384, 4, 16, 256, 1 << 20, 0) == f(1, 1, 16, 256, 16, 0)
