@@ -57,6 +57,15 @@ def parse_args():
                    help="only the chunk append and prefill timing (for counter runs)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="run only a plain device copy of known size (HBM counter calibration)")
+    p.add_argument("--timeline-raw", metavar="FILE.npy", default=None,
+                   help="with --timeline: also save the raw stamps of the live workgroups")
+    p.add_argument("--decode-only", metavar="WORKLOAD", default=None,
+                   choices=["gemma_decode", "sliding_window_decode", "long_context_splitk"],
+                   help="only the decode timing of WORKLOAD (for counter runs)")
+    p.add_argument("--timeline", metavar="WORKLOAD", default=None,
+                   choices=["gemma_decode", "sliding_window_decode"],
+                   help="per-workgroup phase breakdown of one decode launch of WORKLOAD; needs "
+                        "the timeline build (PKV_LIBRARY=block_paged_kv_append_amd/libpkv_timeline.so)")
     return p.parse_args()
 
 
@@ -136,8 +145,11 @@ class DecodeBench:
 
         self.case, self.torch, self.pkv = case, torch, pkv
         dt = case.dtype
-        pool_bytes = case.k_pool.nbytes + case.v_pool.nbytes
-        R = replicas or max(2, math.ceil((1 << 30) / pool_bytes))
+        # enough replicas that 1 GiB is read between two reads of one
+        # replica: a call's K/V then comes from HBM, not the 256 MB
+        # Infinity Cache (as one layer's cache in an engine, read once per
+        # step between the other layers')
+        R = replicas or max(2, math.ceil((1 << 30) / decode_bytes(case)))
         self.R = R
         kp = pkv.from_bits(case.k_pool, dt)
         vp = pkv.from_bits(case.v_pool, dt)
@@ -478,6 +490,109 @@ def calibrate_copy(torch):
 
 
 # ---------------------------------------------------------------------------
+# timeline: where one decode launch spends its time (timeline build only)
+# ---------------------------------------------------------------------------
+TL_WGS, TL_STAMPS = 4096, 32  # the library's timeline buffer geometry
+
+
+def timeline(name, torch, pkv, wl, replays=40, raw_out=None):
+    """Phase stamps of every workgroup of one decode launch of the named
+    workload, taken by the timeline build of the library (s_memrealtime, one
+    lane per workgroup; the block-loop end per wave).  The launch is the last
+    of a graph of calls over the pool replicas, replayed like the bench's
+    timed steps (the Gemma-style workload runs its fused tick)."""
+    import ctypes
+
+    import numpy as np
+
+    lib = pkv.load_library()
+    if not hasattr(lib, "pkv_timeline_set"):
+        raise SystemExit("--timeline needs the timeline build: "
+                         "PKV_LIBRARY=block_paged_kv_append_amd/libpkv_timeline.so")
+    lib.pkv_timeline_set.argtypes = [ctypes.c_void_p]
+    lib.pkv_timeline_set.restype = None
+    lib.pkv_timeline_clock_khz.restype = ctypes.c_int
+    khz = lib.pkv_timeline_clock_khz()
+    case = getattr(wl, name)()
+    b = DecodeBench(case, 0, torch, pkv)
+    op = b.tick if name == "gemma_decode" else b.decode
+    buf = torch.zeros(TL_WGS * TL_STAMPS, dtype=torch.int64, device="cuda")
+    lib.pkv_timeline_set(buf.data_ptr())
+
+    def calls():
+        for r in range(b.R):
+            op(r)
+
+    calls()
+    torch.cuda.synchronize()
+    g = capture(torch, calls)
+    warm(g, torch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    buf.zero_()
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    per_call_us = e0.elapsed_time(e1) * 1e3 / (replays * b.R)
+    lib.pkv_timeline_set(None)
+    st = buf.view(TL_WGS, TL_STAMPS).cpu().numpy().astype(np.int64)
+    live = (st[:, 11] != 0) & (st[:, 2] != 0)  # workgroups that ran a piece
+    s = st[live]
+    t0 = s[:, 0].min()
+    us = lambda col: (s[:, col] - t0) * 1e3 / khz  # noqa: E731
+    loop_end = (s[:, 4:8].max(axis=1) - t0) * 1e3 / khz
+    loop_first = (s[:, 4:8].min(axis=1) - t0) * 1e3 / khz
+    # count-in and merge of the last piece (stamps of an earlier piece are older than its combine)
+    merged = s[:, 10] > s[:, 8]
+
+    def pct(x):
+        x = np.asarray(x, dtype=np.float64)
+        if x.size == 0:
+            return None
+        return {k: round(float(np.percentile(x, q)), 2)
+                for k, q in (("min", 0), ("p10", 10), ("p50", 50), ("p90", 90), ("max", 100))}
+
+    split = s[:, 9] > s[:, 8]  # the last piece was split: it counted in
+    xcd = np.nonzero(live)[0] % 8
+    res = {
+        "timeline": name, "workgroups": int(live.sum()), "clock_khz": khz,
+        "per_call_us_events": round(per_call_us, 2),
+        "span_us": round(float(us(11).max()), 2),
+        "phases_us_from_first_entry": {
+            "entry": pct(us(0)), "setup_done": pct(us(1)), "first_copies_issued": pct(us(2)),
+            "first_block_landed": pct(us(3)), "block_loop_done_last_wave": pct(loop_end),
+            "waves_combined": pct(us(8)), "count_in_done": pct(us(9)[split]),
+            "merge_done": pct(us(10)[merged]), "exit": pct(us(11))},
+        "durations_us": {
+            "setup": pct(us(1) - us(0)), "setup_to_first_copy": pct(us(2) - us(1)),
+            "first_copy_latency": pct(us(3) - us(2)),
+            "wave_spread_at_loop_end": pct(loop_end - loop_first),
+            "combine_after_last_wave": pct(us(8) - loop_end),
+            "count_in": pct((us(9) - us(8))[split]),
+            "merge": pct((us(10) - us(9))[merged]),
+            "first_piece_entry_to_issue_loop": pct(us(13) - us(12)),
+            "first_piece_issue_loop": pct(us(2) - us(13)),
+            "first_piece_table_and_q_wait": pct(us(16) - us(13)),
+            "first_piece_copy_issue": pct(us(2) - us(16)),
+            "combine_barrier_after_last_wave": pct(us(17) - loop_end),
+            "combine_lds_write": pct(us(18) - us(17)),
+            "combine_fold_and_store": pct(us(8) - us(18)),
+            "count_in_store_wait": pct((us(19) - us(8))[split]),
+            "count_in_atomic": pct((us(9) - us(19))[split]),
+            "second_piece_entry_to_copies_issued": pct((us(15) - us(14))[s[:, 14] != 0])},
+        "merging_workgroups": int(merged.sum()),
+        "two_piece_workgroups": int((s[:, 14] != 0).sum()),
+        "entry_by_xcd_us": {int(x): pct(us(0)[xcd == x]) for x in range(8)},
+    }
+    if raw_out:
+        np.save(raw_out, st[live])
+    del b
+    torch.cuda.empty_cache()
+    return res
+
+
+# ---------------------------------------------------------------------------
 # CPU baseline: the oracle on the host cores
 # ---------------------------------------------------------------------------
 def cpu_baseline(case, budget_s):
@@ -523,6 +638,18 @@ def main():
     from block_paged_kv_append_amd import workloads as wl
 
     pkv.load_library()  # raises if libpkv.so is missing: there is no fallback
+    if args.timeline:
+        print(json.dumps(timeline(args.timeline, torch, pkv, wl, raw_out=args.timeline_raw)),
+              flush=True)
+        return
+    if args.decode_only:
+        c = getattr(wl, args.decode_only)()
+        b = DecodeBench(c, 0, torch, pkv)
+        ms = time_decode_op(b, 20, torch)
+        print(json.dumps({"decode_only": c.name, "ms": round(ms, 5),
+                          "gbs": round(decode_bytes(c) / (ms * 1e-3) / 1e9, 1),
+                          "algorithmic_bytes": decode_bytes(c), "pool_replicas": b.R}))
+        return
     if args.calibrate_copy:
         calibrate_copy(torch)
         return

@@ -19,7 +19,8 @@ import threading
 from typing import Optional
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libpkv.so")
+# PKV_LIBRARY selects another build of the library (e.g. libpkv_timeline.so)
+LIB_PATH = os.environ.get("PKV_LIBRARY") or os.path.join(PKG_DIR, "libpkv.so")
 
 PKV_F32 = 0
 PKV_BF16 = 1

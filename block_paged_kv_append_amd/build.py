@@ -52,6 +52,9 @@ def _compile(src: str, extra) -> str:
     return obj
 
 
+TIMELINE_LIB = os.path.join(PKG, "libpkv_timeline.so")
+
+
 def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
     """Compile every source for gfx950 and link ``libpkv.so``.  Always rebuilds."""
     os.makedirs(BUILD, exist_ok=True)
@@ -68,5 +71,19 @@ def build(extra_flags=(), out: str = LIB, verbose: bool = False) -> str:
     return out
 
 
+def build_timeline(verbose: bool = False) -> str:
+    """The timeline build: the same library, with the decode kernels writing
+    per-workgroup phase stamps (``bench.py --timeline`` reads them)."""
+    global BUILD
+    saved, BUILD = BUILD, os.path.join(PKG, "_build_timeline")
+    try:
+        return build(extra_flags=["-DPKV_TIMELINE"], out=TIMELINE_LIB, verbose=verbose)
+    finally:
+        BUILD = saved
+
+
 if __name__ == "__main__":
-    build(extra_flags=sys.argv[1:], verbose=True)
+    if sys.argv[1:] == ["--timeline"]:
+        build_timeline(verbose=True)
+    else:
+        build(extra_flags=sys.argv[1:], verbose=True)

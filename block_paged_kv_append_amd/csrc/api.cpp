@@ -17,6 +17,11 @@ namespace {
 
 thread_local char g_err[512] = "";
 
+#ifdef PKV_TIMELINE
+// timeline build: where the decode kernels write their phase stamps
+unsigned long long* g_timeline = nullptr;
+#endif
+
 int fail(int code, const char* fmt, ...) {
   va_list ap;
   va_start(ap, fmt);
@@ -158,6 +163,9 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const Deco
   a.scores = x.scores;
   a.column_mass = x.column_mass;
   a.score_stride = x.score_stride;
+#ifdef PKV_TIMELINE
+  a.timeline = g_timeline;
+#endif
   a.block_tables = block_tables;
   a.context_lens = context_lens;
   a.num_blocks = num_blocks;
@@ -192,9 +200,12 @@ int decode_impl(const char* fn, void* out, float* lse, const void* q, const Deco
     a.part_blocks = partition_size / PKV_BLOCK_SIZE;
     a.num_partitions = np > 0 ? np : 1;
     a.num_workers = (int32_t)grid;
+    a.units32 = grid < (1LL << 31) ? 1 : 0;
   } else {
     a.units_bound =
         (long long)num_seqs * num_kv_heads * max_units_per_seq(max_context_len, window, x.sink);
+    // the split adds at most 64 cost units per segment
+    a.units32 = a.units_bound + (long long)num_seqs * num_kv_heads * 64 < (1LL << 31) ? 1 : 0;
     a.part_blocks = 0;
     a.num_partitions = 0;
     a.num_workers = 0;  // chosen by launch_decode for the kernel variant
@@ -289,6 +300,19 @@ int device_scratch(const char* fn, hipStream_t stream, void** out) {
 extern "C" {
 
 const char* pkv_last_error(void) { return g_err; }
+
+#ifdef PKV_TIMELINE
+// Timeline build only (not declared in pkv.h): the device buffer of
+// kTimelineWgs x kTimelineStamps words the next decode launches stamp (NULL:
+// none), and the stamp clock's rate in kHz.
+void pkv_timeline_set(unsigned long long* buf) { g_timeline = buf; }
+int pkv_timeline_clock_khz(void) {
+  int dev = 0, khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess) return 0;
+  return khz;
+}
+#endif
 
 int paged_kv_append(const void* k_new, const void* v_new, const int32_t* slot_mapping,
                     int32_t num_tokens, void* k_pool, void* v_pool, int32_t num_blocks,

@@ -105,6 +105,19 @@ __device__ __forceinline__ long long wave_sum_i64(long long v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
   return v;
 }
+// Inclusive prefix sum over the 64 lanes in six DPP steps (no LDS round
+// trips): row-local Hillis-Steele shifts by 1, 2, 4, 8 within each row of 16
+// lanes, then the last lane of row 0 (2) added to row 1 (3), and the last
+// lane of row 1 to rows 2 and 3.  The sum must fit in 32 bits.
+__device__ __forceinline__ int wave_incl_scan_i32(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, true);   // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, true);   // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, true);   // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, true);   // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
+  return x;
+}
 __device__ __forceinline__ long long wave_incl_scan_i64(long long v, int lane) {
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {

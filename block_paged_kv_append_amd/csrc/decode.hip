@@ -60,12 +60,41 @@ __device__ __forceinline__ float load_dev(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Timeline build (PKV_TIMELINE): a workgroup's phases as s_memrealtime
+// stamps, written by one lane to a.timeline[blockIdx.x][k]:
+//   0 entry, 1 set-up done, 2 first piece's first copies issued (wave 0),
+//   3 its first block landed (wave 0), 4 + w last piece's block loop done
+//   (wave w), 8 its waves combined, 9 its count-in done, 10 its merge done,
+//   11 exit; 12 first piece entered, 13 its copies about to be issued;
+//   14 second piece entered, 15 its first copies issued; 16 first piece:
+//   its table slice and query fragments have landed (the timeline build
+//   waits for them there, before the first copy); last piece: 17 all waves
+//   at the combine, 18 their partial outputs in LDS, 19 its partial stores
+//   done (count-in), 20 merge: partials loaded.
+#ifdef PKV_TIMELINE
+__device__ __forceinline__ void tl_put(const DecodeArgs& a, int k, unsigned long long v) {
+  if (a.timeline != nullptr && blockIdx.x < (unsigned)kTimelineWgs)
+    a.timeline[(size_t)blockIdx.x * kTimelineStamps + k] = v;
+}
+#define PKV_TL(a, k) \
+  do { if (threadIdx.x == 0) tl_put(a, k, __builtin_amdgcn_s_memrealtime()); } while (0)
+#define PKV_TL_WAVE(a, k) \
+  do { if ((threadIdx.x & 63) == 0) tl_put(a, (k) + (int)(threadIdx.x >> 6), __builtin_amdgcn_s_memrealtime()); } while (0)
+#define PKV_TL_VAL(a, k, v) \
+  do { if (threadIdx.x == 0) tl_put(a, k, (unsigned long long)(v)); } while (0)
+#else
+#define PKV_TL(a, k) ((void)0)
+#define PKV_TL_WAVE(a, k) ((void)0)
+#define PKV_TL_VAL(a, k, v) ((void)0)
+#endif
+
 struct Piece {
   int b, g;       // sequence, kv head
   SeqSpan sp;     // its visible range
   int j0, j1;     // blocks [j0, j1) of the segment's visible blocks
   int slot;       // workspace slot if partial
   long long S;    // flattened index of the segment's first unit (balanced mode)
+  int ord = 0;    // pieces of this workgroup before it (timeline build)
 };
 
 // Fused append (paged_attn_decode_append).  Sequence b's newest token sits
@@ -688,6 +717,10 @@ constexpr int kPieceCost = PKV_DECODE_PIECE_COST_BYTES / (2 * kBlock * D * 2);
 template <int D, bool FUSE, bool EVICT>
 __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const Piece& pc,
                                float* lds) {
+#ifdef PKV_TIMELINE
+  if (pc.ord == 0) PKV_TL(a, 12);
+  if (pc.ord == 1) PKV_TL(a, 14);
+#endif
   constexpr int KS = D / 32;                        // score products
   constexpr int XT = D / 16;                        // output tiles
   constexpr int kTileBytes = D * kBlock * 2;        // one block's K (or V)
@@ -707,13 +740,16 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   sp.L = __builtin_amdgcn_readfirstlane(pc.sp.L);
   const SinkPart sk = EVICT ? sink_part(sp, a.window, a.sink) : SinkPart{0, 0};
 
+  // query fragments: every lane loads from a real row (columns past the
+  // group read its last row), then columns past the group are zeroed, so the
+  // loads need no branches
   u32x4 qf[KS];
   {
     const uint16_t* qrow =
         reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * Hq + g * G + min(c, G - 1)) * D + 8 * j;
+    const uint32_t keep = c < G ? 0xFFFFFFFFu : 0u;
 #pragma unroll
-    for (int s = 0; s < KS; ++s)
-      qf[s] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < KS; ++s) qf[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s) & keep;
   }
 
   f32x4 o[XT];
@@ -738,6 +774,13 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   NewToken<2, D> nt;
   if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
   uint32_t okbits = 0;  // bit (block % NS): that slot's block was readable
+#ifdef PKV_TIMELINE
+  if (pc.ord == 0) {
+    PKV_TL(a, 13);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    PKV_TL(a, 16);
+  }
+#endif
 
   // copy this wave's block i (past the end: an empty range, zeros) into its slot
   auto issue = [&](int i) {
@@ -765,11 +808,18 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
 
 #pragma unroll
   for (int i = 0; i < NS; ++i) issue(i);
+#ifdef PKV_TIMELINE
+  if (pc.ord == 0) PKV_TL(a, 2);
+  if (pc.ord == 1) PKV_TL(a, 15);
+#endif
   for (int i = 0; i < nw; ++i) {
     // block i has landed: the NS - 1 later blocks may still be in flight
     constexpr int kAfter = (NS - 1) * kRuns;
     __builtin_amdgcn_s_waitcnt((kAfter & 15) | ((kAfter >> 4) << 14) | (7 << 4) | (15 << 8));
     asm volatile("" ::: "memory");
+#ifdef PKV_TIMELINE
+    if (pc.ord == 0 && i == 0) PKV_TL(a, 3);
+#endif
     const int slot = i % NS;
     const bool ok = (okbits >> slot) & 1u;
     const char* kt = ring + slot * 2 * kTileBytes;
@@ -784,11 +834,13 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
     issue(i + NS);  // into the slot just read (the products have their operands)
   }
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the copies past the end have landed
+  PKV_TL_WAVE(a, 4);
 
   // ---- combine the four waves through LDS (the rings are free now) ----
   mma_result_fence();
   const float l_tot = quad_sum(l_run);
   __syncthreads();
+  PKV_TL(a, 17);
   float* lo = lds;                    // [4][G][D]
   float* lml = lds + kWaves * G * D;  // [4][G][2]
   if (c < G) {
@@ -801,8 +853,10 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
     }
   }
   __syncthreads();
+  PKV_TL(a, 18);
   combine_waves<true, D, EVICT>(a, pc, lo, lml);
   __syncthreads();  // LDS is reused by the next piece
+  PKV_TL(a, 8);
 }
 
 // ---------------------------------------------------------------------------
@@ -904,14 +958,14 @@ __device__ void run_piece_stream(const DecodeArgs& a, const LogitXform& xf, cons
         reinterpret_cast<const uint16_t*>(a.q) + ((size_t)b * Hq + g * G + min(c, G - 1)) * D + 8 * j;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      qf[s] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+      qf[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s) & (c < G ? 0xFFFFFFFFu : 0u);
   }
   if (has_nx) {
     const uint16_t* qrow =
         reinterpret_cast<const uint16_t*>(a.q) + ((size_t)nb_ * Hq + ng * G + min(c, G - 1)) * D + 8 * j;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
-      rs.qn[s] = c < G ? *reinterpret_cast<const u32x4*>(qrow + 32 * s) : u32x4{0, 0, 0, 0};
+      rs.qn[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s) & (c < G ? 0xFFFFFFFFu : 0u);
   }
   NewToken<2, D> nt;
   if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
@@ -1037,6 +1091,7 @@ template <bool BF16, int D, bool V, typename SlotList>
 __device__ void finish_split(const DecodeArgs& a, int b, int g, SlotList slots, float* lds, int k = 1) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this thread's partial stores are done
   __syncthreads();
+  PKV_TL(a, 19);
   int* cnt = a.seg_count + (size_t)b * a.num_kv_heads + g;
   int* flag = reinterpret_cast<int*>(lds);
   if (threadIdx.x == 0)
@@ -1044,10 +1099,12 @@ __device__ void finish_split(const DecodeArgs& a, int b, int g, SlotList slots, 
   __syncthreads();
   const bool last = flag[0] != 0;
   __syncthreads();  // LDS is reused below
+  PKV_TL(a, 9);
   if (!last) return;
   merge_segment<BF16, D, SlotList, V>(a, b, g, slots, lds);
   if (threadIdx.x == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __syncthreads();
+  PKV_TL(a, 10);
 }
 
 // Split-K decode, persistent form (see run_piece_stream): workgroup w of N
@@ -1094,27 +1151,57 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fixed_stream_kernel(Decode
   for (int b = w; b < B; b += N)  // sequences with no visible token
     if (span(len_of(b)).nb == 0) write_empty<true, D, false>(a, b, 0, Hkv * G);
 
-  long long I = 0;
-  for (int r = 0; r * kWave < B; ++r) I += wave_sum_i64(parts(len_at(r)));
-  I *= Hkv;
-  const long long i0 = __builtin_amdgcn_readfirstlane((long long)w * I / N);
-  const long long i1 = (long long)(w + 1) * I / N;
-  if (i0 >= i1) return;
-
-  // segment holding item i0: first sequence whose inclusive prefix exceeds i0
-  long long run = 0, seg_base = 0;
+  long long I = 0, i0 = 0, i1 = 0, seg_base = 0;
   int b0 = 0;
-  for (int r = 0; r * kWave < B; ++r) {
-    const long long nph = (long long)parts(len_at(r)) * Hkv;
-    const long long incl = wave_incl_scan_i64(nph, lane);
-    const unsigned long long hit = __ballot(run + incl > i0);
-    if (hit) {
-      const int l0 = __ffsll(hit) - 1;
-      b0 = r * kWave + l0;
-      seg_base = run + __shfl(incl - nph, l0);
-      break;
+  if (B <= kLenRegs * kWave && a.units32) {
+    // as the balanced split's set-up: one DPP scan per 64 sequences
+    int incl[kLenRegs], tot[kLenRegs], own[kLenRegs];
+#pragma unroll
+    for (int r = 0; r < kLenRegs; ++r) {
+      incl[r] = tot[r] = own[r] = 0;
+      if (r * kWave < B) {
+        own[r] = parts(Lr[r]) * Hkv;
+        incl[r] = wave_incl_scan_i32(own[r]);
+        tot[r] = __builtin_amdgcn_readlane(incl[r], kWave - 1);
+        I += tot[r];
+      }
     }
-    run += __shfl(incl, kWave - 1);
+    i0 = __builtin_amdgcn_readfirstlane((long long)w * I / N);
+    i1 = (long long)(w + 1) * I / N;
+    if (i0 >= i1) return;
+    long long run = 0;
+#pragma unroll
+    for (int r = 0; r < kLenRegs; ++r) {
+      if (r * kWave >= B) break;
+      const unsigned long long hit = __ballot(run + incl[r] > i0);
+      if (hit) {
+        const int l0 = __ffsll(hit) - 1;
+        b0 = r * kWave + l0;
+        seg_base = run + __builtin_amdgcn_readlane(incl[r] - own[r], l0);
+        break;
+      }
+      run += tot[r];
+    }
+  } else {
+    for (int r = 0; r * kWave < B; ++r) I += wave_sum_i64(parts(len_at(r)));
+    I *= Hkv;
+    i0 = __builtin_amdgcn_readfirstlane((long long)w * I / N);
+    i1 = (long long)(w + 1) * I / N;
+    if (i0 >= i1) return;
+    // segment holding item i0: first sequence whose inclusive prefix exceeds i0
+    long long run = 0;
+    for (int r = 0; r * kWave < B; ++r) {
+      const long long nph = (long long)parts(len_at(r)) * Hkv;
+      const long long incl = wave_incl_scan_i64(nph, lane);
+      const unsigned long long hit = __ballot(run + incl > i0);
+      if (hit) {
+        const int l0 = __ffsll(hit) - 1;
+        b0 = r * kWave + l0;
+        seg_base = run + __shfl(incl - nph, l0);
+        break;
+      }
+      run += __shfl(incl, kWave - 1);
+    }
   }
   seg_base = __builtin_amdgcn_readfirstlane(seg_base);
 
@@ -1231,6 +1318,10 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int blk, float*
     const int N = a.num_workers, w = blk;
     const int lane = threadIdx.x & 63;
     const int B = a.num_seqs;
+    PKV_TL(a, 0);
+#ifdef PKV_TIMELINE
+    int tl_pieces = 0;
+#endif
 
     // Context lengths of sequences 64 r + lane, r < kLenRegs, held in
     // registers: one load for the whole set-up below (the work total, the
@@ -1268,28 +1359,62 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int blk, float*
     // units.  Every wave computes the same W.
     constexpr int C = kPieceCost<D>;
     auto seg_units = [&](int nb) -> long long { return nb > 0 ? (long long)(nb + C) : 0; };
-    long long W = 0;
-    for (int r = 0; r * kWave < B; ++r) W += wave_sum_i64(seg_units(span(len_at(r)).nb));
-    W *= Hkv;
-    const long long a0 = (long long)w * W / N, a1 = (long long)(w + 1) * W / N;
-    if (a0 >= a1) return;
-
-    // segment holding unit a0: first sequence whose inclusive prefix exceeds a0
-    long long run = 0, seg_base = 0;
+    long long W = 0, a0 = 0, a1 = 0, seg_base = 0;
     int b0 = 0, L0 = 0;
-    for (int r = 0; r * kWave < B; ++r) {
-      const int Lb = len_at(r);
-      const long long nbh = seg_units(span(Lb).nb) * Hkv;
-      const long long incl = wave_incl_scan_i64(nbh, lane);
-      const unsigned long long hit = __ballot(run + incl > a0);
-      if (hit) {
-        const int l0 = __ffsll(hit) - 1;
-        b0 = r * kWave + l0;
-        L0 = __builtin_amdgcn_readlane(Lb, l0);
-        seg_base = run + __shfl(incl - nbh, l0);
-        break;
+    if (B <= kLenRegs * kWave && a.units32) {
+      // the lengths are all in registers and every total fits in 31 bits:
+      // one DPP scan per 64 sequences gives both the work total and, with a
+      // ballot, the segment holding unit a0 (no LDS round trips)
+      int incl[kLenRegs], tot[kLenRegs];
+#pragma unroll
+      for (int r = 0; r < kLenRegs; ++r) {
+        incl[r] = tot[r] = 0;
+        if (r * kWave < B) {
+          incl[r] = wave_incl_scan_i32((int)seg_units(span(Lr[r]).nb) * Hkv);
+          tot[r] = __builtin_amdgcn_readlane(incl[r], kWave - 1);
+          W += tot[r];
+        }
       }
-      run += __shfl(incl, kWave - 1);
+      a0 = (long long)w * W / N;
+      a1 = (long long)(w + 1) * W / N;
+      if (a0 >= a1) return;
+      long long run = 0;
+#pragma unroll
+      for (int r = 0; r < kLenRegs; ++r) {
+        if (r * kWave >= B) break;
+        const unsigned long long hit = __ballot(run + incl[r] > a0);
+        if (hit) {
+          const int l0 = __ffsll(hit) - 1;
+          b0 = r * kWave + l0;
+          L0 = __builtin_amdgcn_readlane(Lr[r], l0);
+          const int own = (int)seg_units(span(L0).nb) * Hkv;
+          seg_base = run + __builtin_amdgcn_readlane(incl[r], l0) - own;
+          break;
+        }
+        run += tot[r];
+      }
+    } else {
+      for (int r = 0; r * kWave < B; ++r) W += wave_sum_i64(seg_units(span(len_at(r)).nb));
+      W *= Hkv;
+      a0 = (long long)w * W / N;
+      a1 = (long long)(w + 1) * W / N;
+      if (a0 >= a1) return;
+      // segment holding unit a0: first sequence whose inclusive prefix exceeds a0
+      long long run = 0;
+      for (int r = 0; r * kWave < B; ++r) {
+        const int Lb = len_at(r);
+        const long long nbh = seg_units(span(Lb).nb) * Hkv;
+        const long long incl = wave_incl_scan_i64(nbh, lane);
+        const unsigned long long hit = __ballot(run + incl > a0);
+        if (hit) {
+          const int l0 = __ffsll(hit) - 1;
+          b0 = r * kWave + l0;
+          L0 = __builtin_amdgcn_readlane(Lb, l0);
+          seg_base = run + __shfl(incl - nbh, l0);
+          break;
+        }
+        run += __shfl(incl, kWave - 1);
+      }
     }
 
     Piece pc;
@@ -1298,6 +1423,7 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int blk, float*
     pc.g = (int)((a0 - seg_base) / (pc.sp.nb + C));
     long long Sv = seg_base + (long long)pc.g * (pc.sp.nb + C);  // segment start (cost units)
     bool first = true;
+    PKV_TL(a, 1);
     while (true) {
       const long long S = Sv + C, E = S + pc.sp.nb;  // the segment's real units
       const long long lo = max(a0, S), hi = min(a1, E);
@@ -1306,6 +1432,9 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int blk, float*
         pc.j0 = (int)(lo - S);
         pc.j1 = (int)(hi - S);
         pc.slot = first ? 2 * w : 2 * w + 1;
+#ifdef PKV_TIMELINE
+        pc.ord = tl_pieces++;
+#endif
         run_one(xf, pc);
         if (!(pc.j0 == 0 && pc.j1 == pc.sp.nb))
           finish_split<BF16, D, EVICT>(a, pc.b, pc.g, BalancedSlots{W, S, E, Sv, N}, lds);
@@ -1316,11 +1445,13 @@ __device__ __forceinline__ void decode_body(const DecodeArgs& a, int blk, float*
       if (++pc.g == Hkv) {
         pc.g = 0;
         do {
-          if (++pc.b >= B) return;
+          if (++pc.b >= B) break;
           pc.sp = span(a.context_lens[pc.b]);
         } while (pc.sp.nb == 0);
+        if (pc.b >= B) break;
       }
     }
+    PKV_TL(a, 11);
   }
 }
 

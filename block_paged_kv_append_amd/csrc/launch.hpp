@@ -59,6 +59,7 @@ struct DecodeArgs {
   // work decomposition
   int32_t cu_count;         // compute units of the device
   long long units_bound;    // upper bound on (sequence, kv head, block) units
+  int32_t units32;          // 1: the split's unit (or item) totals fit in 31 bits
   int32_t num_workers;      // grid size (set by launch_decode in balanced mode)
   int32_t part_blocks;      // 0: balanced split of all blocks; > 0: fixed partitions of this many blocks
   int32_t num_partitions;   // fixed partitions per sequence
@@ -70,7 +71,14 @@ struct DecodeArgs {
   int32_t score_stride;
   float* scores;
   float* column_mass;
+  // timeline build (PKV_TIMELINE) only: per-workgroup phase stamps
+  // [kTimelineWgs][kTimelineStamps]; null otherwise, and never written
+  unsigned long long* timeline;
 };
+
+// Timeline build: stamps per workgroup, and workgroups recorded.
+constexpr int kTimelineStamps = 32;
+constexpr int kTimelineWgs = 4096;
 
 struct PrefillArgs {
   void* out;
