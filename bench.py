@@ -50,7 +50,8 @@ def parse_args():
     p.add_argument("--steps", type=int, default=200)
     p.add_argument("--warmup", type=int, default=300)
     p.add_argument("--replicas", type=int, default=0, help="pool replicas (0: enough for 1 GiB)")
-    p.add_argument("--cpu-seconds", type=float, default=12.0, help="oracle time budget")
+    p.add_argument("--cpu-seconds", type=float, default=6.0,
+                   help="oracle time budget of the headline workload")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--quick", action="store_true", help="headline step only")
     p.add_argument("--prefill-only", action="store_true",
@@ -247,11 +248,12 @@ def time_steps(bench, steps, warmup, step, torch):
 OP_CALLS = 24  # calls per timed graph replay: the replay's own start-up is spread over them
 
 
-def time_decode_op(bench, iters, torch, op=None):
+def time_decode_op(bench, iters, torch, op=None, spread=None):
     """Average duration of one decode operation (``op(r)``, by default the
     plain decode): a graph of about OP_CALLS calls cycling over the R pool
     replicas, replayed ``iters`` times, each replay bracketed by HIP events on
-    the stream, divided by the calls per replay."""
+    the stream, divided by the calls per replay.  With a dict ``spread``,
+    also the 10th and 90th percentiles of those per-replay means."""
     import numpy as np
 
     op = op or bench.decode
@@ -273,14 +275,19 @@ def time_decode_op(bench, iters, torch, op=None):
         g.replay()
         ev[i][1].record()
     torch.cuda.synchronize()
-    return float(np.mean([a.elapsed_time(b) for a, b in ev])) / (rounds * bench.R)
+    per_call = np.array([a.elapsed_time(b) for a, b in ev]) / (rounds * bench.R)
+    if spread is not None:  # p10 / p90 of the per-call means of the replays
+        spread.update(p10_ms=round(float(np.percentile(per_call, 10)), 5),
+                      p90_ms=round(float(np.percentile(per_call, 90)), 5),
+                      replays=iters, calls_per_replay=rounds * bench.R)
+    return float(np.mean(per_call))
 
 
 APPEND_REPEAT = 16  # appends per graph replay: one alone is shorter than a launch
 PREFILL_REPEAT = 8  # prefills per graph replay (each recomputes the same output)
 
 
-def time_prefill(case, iters, warmup, torch, pkv):
+def time_prefill(case, iters, warmup, torch, pkv, spread=None):
     """Average durations of the chunk append and of the prefill, each replayed
     from its own graph and bracketed by HIP events."""
     import numpy as np
@@ -321,8 +328,13 @@ def time_prefill(case, iters, warmup, torch, pkv):
             g.replay()
             ev[i][1].record()
         torch.cuda.synchronize()
-        res.append(float(np.mean([a.elapsed_time(b) for a, b in ev])))
-    return res[0] / APPEND_REPEAT, res[1] / PREFILL_REPEAT
+        res.append(np.array([a.elapsed_time(b) for a, b in ev]))
+    app, pre = res[0] / APPEND_REPEAT, res[1] / PREFILL_REPEAT
+    if spread is not None:
+        for k, v in (("append", app), ("prefill", pre)):
+            spread[k] = {"p10_ms": round(float(np.percentile(v, 10)), 5),
+                         "p90_ms": round(float(np.percentile(v, 90)), 5)}
+    return float(np.mean(app)), float(np.mean(pre))
 
 
 COPY_PAIRS = 512  # copy-on-write pairs per call in the block-copy measurement
@@ -476,6 +488,28 @@ def copy_rate(torch) -> float:
     return 2 * n / (ms * 1e-3) / 1e9
 
 
+def read_rate(torch, pkv) -> float:
+    """GB/s of a plain read of 2 GiB (the library's read probe, 8 workgroups
+    per compute unit): the HBM read rate a kernel reaches on this GPU right
+    now, the practical ceiling of the decode."""
+    n = 2 << 30
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(3)
+    out = torch.empty(8 * torch.cuda.get_device_properties(0).multi_processor_count,
+                      dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        pkv.hbm_read_probe(buf, out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        pkv.hbm_read_probe(buf, out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del buf, out
+    torch.cuda.empty_cache()
+    return n / (ms * 1e-3) / 1e9
+
+
 def calibrate_copy(torch):
     """A plain device-to-device copy of 1 GiB, 10 times: the reference for
     scaling the HBM FETCH_SIZE / WRITE_SIZE counters."""
@@ -595,30 +629,63 @@ def timeline(name, torch, pkv, wl, replays=40, raw_out=None):
 # ---------------------------------------------------------------------------
 # CPU baseline: the oracle on the host cores
 # ---------------------------------------------------------------------------
-def cpu_baseline(case, budget_s):
+def _host_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        return len(os.sched_getaffinity(0))
+
+
+def cpu_baseline(case, budget_s, runs=None):
+    """The float64 oracle's decode of the whole workload on the host cores:
+    passes until ``budget_s`` seconds (or exactly ``runs`` passes, the median
+    reported), as algorithmic GB/s."""
     import numpy as np
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = len(os.sched_getaffinity(0))
+    threads = _host_threads()
     per_pass = decode_bytes(case)
-    passes, t0 = 0, time.perf_counter()
+    times, t0 = [], time.perf_counter()
     while True:
+        t = time.perf_counter()
         oracle.decode(case.q, case.k_pool, case.v_pool, case.block_tables, case.context_lens,
                       case.scale, case.softcap, case.window, case.dtype)
-        passes += 1
+        times.append(time.perf_counter() - t)
         el = time.perf_counter() - t0
-        if el >= budget_s or passes >= 1000:
+        if (runs and len(times) >= runs) or (not runs and (el >= budget_s or len(times) >= 1000)):
             break
-    return {"value": round(per_pass * passes / el / 1e9, 4), "unit": "GB/s",
-            "cores": int(threads), "kind": "oracle",
-            "sample": f"full workload (all {case.num_seqs} sequences), {passes} passes in "
-                      f"{el:.1f} s; float64 numpy, BLAS threads {threads}, "
+    if runs:
+        sec = float(np.median(times))
+        how = f"median of {len(times)} passes over the full workload (all {case.num_seqs} " \
+              f"sequences), {sec:.2f} s each"
+    else:
+        sec = el / len(times)
+        how = f"full workload (all {case.num_seqs} sequences), {len(times)} passes in {el:.1f} s"
+    return {"value": round(per_pass / sec / 1e9, 4), "unit": "GB/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{how}; float64 numpy, BLAS threads {threads}, "
                       f"host affinity {len(os.sched_getaffinity(0))} cpus"}
+
+
+def cpu_baseline_prefill(case):
+    """The float64 oracle's prefill of the whole chunked-prefill workload (the
+    chunk already appended), one pass, as algorithmic GFLOP/s."""
+    import oracle
+
+    threads = _host_threads()
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           case.dtype)
+    t = time.perf_counter()
+    oracle.prefill(case.q, case.cu_q_lens, kr, vr, case.block_tables, case.context_lens,
+                   case.scale, case.softcap, case.window, case.dtype)
+    sec = time.perf_counter() - t
+    return {"value": round(prefill_flops(case) / sec / 1e9, 3), "unit": "GFLOP/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"one pass over the full workload (all {case.num_seqs} chunks), {sec:.2f} s; "
+                      f"float64 numpy, BLAS threads {threads}, host affinity "
+                      f"{len(os.sched_getaffinity(0))} cpus"}
 
 
 # ---------------------------------------------------------------------------
@@ -669,7 +736,8 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
     tbytes = tick_bytes(case)
     value = tbytes / (ms_per_step * 1e-3) / 1e9
-    kern_avg_ms = time_decode_op(bench, max(10, args.steps // bench.R), torch, bench.tick)
+    kspread = {}
+    kern_avg_ms = time_decode_op(bench, max(10, args.steps // bench.R), torch, bench.tick, kspread)
     achieved = tbytes / (kern_avg_ms * 1e-3) / 1e9
     traffic = measured_traffic("decode")
     line = {
@@ -697,7 +765,8 @@ def main():
                      "traffic": traffic,
                      "kernel": "paged_attn_decode_append: decode_kernel (balanced split, "
                                "fused append, in-launch merge)",
-                     "kernel_ms": round(kern_avg_ms, 5), "algorithmic_bytes": tbytes},
+                     "kernel_ms": round(kern_avg_ms, 5), "kernel_spread": kspread,
+                     "algorithmic_bytes": tbytes},
     }
 
     if not args.quick:
@@ -710,20 +779,25 @@ def main():
                               "decode_only_gbs": round(decode_bytes(case) / (dec_ms * 1e-3) / 1e9, 1)}
         extra = {}
         pc = wl.chunked_prefill_shared_prefix()
-        app_ms, pre_ms = time_prefill(pc, 20, 3, torch, pkv)
+        pspread = {}
+        app_ms, pre_ms = time_prefill(pc, 40, 3, torch, pkv, pspread)
         flops = prefill_flops(pc)
         tf = flops / (pre_ms * 1e-3) / 1e12
         ab = append_bytes(pc.num_q_tokens, pc.num_kv_heads, pc.head_dim, 2)
         line["prefill"] = {
             "workload": "chunked_prefill_shared_prefix: 8 seqs x (2048 cached, first 1024 shared) "
                         "+ 512-token chunk, 8q/2kv heads, D256, bf16, causal",
-            "tflops": round(tf, 2), "ms": round(pre_ms, 5), "flops": flops,
+            "tflops": round(tf, 2), "ms": round(pre_ms, 5), "spread": pspread["prefill"],
+            "flops": flops,
             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / BF16_MFMA_PEAK_TFLOPS, 4),
                          "traffic": measured_traffic("prefill")},
             "append": {"ms": round(app_ms, 5), "gbs": round(ab / (app_ms * 1e-3) / 1e9, 1),
-                       "bytes": ab},
+                       "hbm_frac": round(ab / (app_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                       "spread": pspread["append"], "bytes": ab},
         }
+        if not args.no_cpu_baseline:
+            line["prefill"]["cpu_baseline"] = cpu_baseline_prefill(pc)
         del pc
         cb_ms, cb_pairs, cb_bytes = time_copy_blocks(bench, 20, torch)
         line["copy_blocks"] = {"pairs": cb_pairs, "ms": round(cb_ms, 5),
@@ -737,12 +811,16 @@ def main():
         for maker in (wl.sliding_window_decode, wl.long_context_splitk):
             c = maker()
             b = DecodeBench(c, 0, torch, pkv)
-            ms = time_decode_op(b, 20, torch)
+            sp = {}
+            ms = time_decode_op(b, 40, torch, spread=sp)
             gbs = decode_bytes(c) / (ms * 1e-3) / 1e9
-            extra[c.name] = {"ms": round(ms, 5), "gbs": round(gbs, 1),
+            extra[c.name] = {"ms": round(ms, 5), "spread": sp, "gbs": round(gbs, 1),
                              "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                              "tok_per_s": round(c.num_seqs / (ms * 1e-3), 1),
+                             "algorithmic_bytes": decode_bytes(c), "pool_replicas": b.R,
                              "entry": "splitk P=%d" % c.partition_size if c.partition_size else "balanced"}
+            if not args.no_cpu_baseline:
+                extra[c.name]["cpu_baseline"] = cpu_baseline(c, 0, runs=1 if c.partition_size else 3)
             del b, c
             torch.cuda.empty_cache()
         line["other_workloads"] = extra
@@ -750,6 +828,9 @@ def main():
 
     if not args.quick:
         line["box_copy_gbs"] = round(copy_rate(torch), 1)
+        rr = read_rate(torch, pkv)
+        line["box_read_gbs"] = round(rr, 1)
+        line["roofline"]["frac_of_box_read"] = round(achieved / rr, 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)

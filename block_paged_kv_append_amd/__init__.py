@@ -65,6 +65,7 @@ SIGNATURES = {
     "paged_attn_mixed": (ctypes.c_int, [_P, _P, _P, _P, _I, _I, _I, _P, _P, _I, _P, _I, _P, _I, _I,
                                         _I, _I, _I, _I, _F, _F, _I, _P, _Z, _I, _P]),
     "pkv_check_paged_metadata": (ctypes.c_int, [_P, _P, _I, _I, _I, _P, _I, _P, _P]),
+    "pkv_hbm_read_probe": (ctypes.c_int, [_P, _Z, _P, _I, _P]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
 
@@ -512,6 +513,21 @@ def paged_attn_prefill(out, q, cu_q_lens, max_q_len, k_pool, v_pool, block_table
 # ---------------------------------------------------------------------------
 # numpy bit arrays <-> device tensors
 # ---------------------------------------------------------------------------
+def hbm_read_probe(buf, out, num_wgs=None, stream=None) -> None:
+    """A plain read of the whole of ``buf`` (a device tensor, its byte size a
+    multiple of 16) by ``num_wgs`` workgroups (default: 8 per compute unit),
+    each writing one word of ``out`` (int32/uint32, >= num_wgs entries): the
+    HBM read rate of a kernel that does nothing else."""
+    import torch
+
+    n = num_wgs or 8 * torch.cuda.get_device_properties(buf.device).multi_processor_count
+    if out.numel() < n or out.element_size() != 4:
+        raise ValueError("out needs num_wgs 32-bit entries")
+    lib = load_library()
+    _check("pkv_hbm_read_probe", lib.pkv_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
+                                                        _ptr(out), int(n), _stream(stream)))
+
+
 def from_bits(bits, dtype: str, device="cuda"):
     """uint16 (bf16) / uint32 (fp32) storage bits -> a device tensor."""
     import numpy as np

@@ -14,7 +14,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpkv.so")
 SOURCES = ["api.cpp", "graph.cpp", "allocator.cpp", "append.hip", "blocks.hip", "decode.hip",
-           "prefill.hip", "mixed.hip", "check.hip"]
+           "prefill.hip", "mixed.hip", "check.hip", "bandwidth.hip"]
 ARCH = os.environ.get("PKV_OFFLOAD_ARCH", "gfx950")
 
 HIPCC_FLAGS = [

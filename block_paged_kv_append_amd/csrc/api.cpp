@@ -370,6 +370,19 @@ int paged_kv_copy_blocks(void* k_pool, void* v_pool, int32_t num_blocks, int32_t
   return from_hip(pkv::launch_copy_blocks(a, reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* out, int32_t num_wgs,
+                       struct ihipStream_t* stream) {
+  const char* fn = "pkv_hbm_read_probe";
+  if (bytes == 0) return PKV_OK;
+  if (buf == nullptr || out == nullptr) return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (bytes % 16 != 0 || !aligned(buf, 16) || !aligned(out, 4))
+    return fail(PKV_EINVAL, "%s: bytes %zu not a multiple of 16, or misaligned pointers", fn,
+                bytes);
+  if (num_wgs < 1 || num_wgs > (1 << 20)) return fail(PKV_EINVAL, "%s: num_wgs %d", fn, num_wgs);
+  return from_hip(pkv::launch_hbm_read(buf, bytes, out, num_wgs,
+                                       reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 int pkv_check_paged_metadata(const int32_t* block_tables, const int32_t* context_lens,
                              int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
                              const int32_t* slot_mapping, int32_t num_slots, uint32_t* flags,

@@ -8,9 +8,11 @@
 // One workgroup moves a tile of 16 consecutive tokens of one kv head.  Rows
 // are read with coalesced 16-byte loads into LDS, then written out with the
 // token index fastest across lanes, which is the contiguous direction of both
-// pools: K chunks [.., 16, X] and V rows [.., D, 16].  When the 16 tokens fill
-// consecutive slots of one block (a prefill chunk) each wave writes whole
-// contiguous runs.
+// pools: K chunks [.., 16, X] and V rows [.., D, 16].  When the 16 tokens
+// fill one block in order (slots 16 n .. 16 n + 15: a prefill chunk), the
+// block's K tile and V tile are each one contiguous run and every lane writes
+// 16-byte pieces of them; otherwise each token is placed on its own (V one
+// element at a time).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -54,7 +56,13 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
   }
   __syncthreads();
 
-  // K: chunk c of token t -> k_pool[blk, g, c, off, :]
+  // the 16 tokens fill one block in order (the same answer in every thread)
+  bool whole = nt == kBlock && slot_of[0] >= 0 && (slot_of[0] & (kBlock - 1)) == 0;
+#pragma unroll
+  for (int t = 1; t < kBlock; ++t) whole &= slot_of[t] == slot_of[0] + t;
+
+  // K: chunk c of token t -> k_pool[blk, g, c, off, :]; for a whole block
+  // the destination index is tile base + idx (one contiguous 16 x D run)
   u32x4* kp = reinterpret_cast<u32x4*>(a.k_pool);
   for (int idx = tid; idx < kBlock * NCH; idx += kAppendThreads) {
     const int t = idx % kBlock, c = idx / kBlock;
@@ -62,6 +70,33 @@ __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs a) {
     if (s < 0) continue;
     const int blk = s / kBlock, off = s % kBlock;
     kp[(((size_t)blk * Hkv + g) * NCH + c) * kBlock + off] = k_tile[t * PITCH + c];
+  }
+
+  if (whole) {
+    // V tile [D][16] of the block, 16 bytes per lane: dim d, tokens X q .. X q + X - 1
+    const size_t base = ((size_t)(slot_of[0] / kBlock) * Hkv + g) * D * kBlock * ES;
+    u32x4* vdst = reinterpret_cast<u32x4*>(reinterpret_cast<char*>(a.v_pool) + base);
+    const char* vt = reinterpret_cast<const char*>(v_tile);
+    constexpr int QPD = kBlock / X;  // 16-byte pieces per dim
+    for (int idx = tid; idx < D * QPD; idx += kAppendThreads) {
+      const int d = idx / QPD, q = idx % QPD;
+      uint32_t w[4];
+      if constexpr (ES == 2) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int t = X * q + 2 * e;
+          const uint32_t lo = *reinterpret_cast<const uint16_t*>(vt + ((size_t)t * PITCH * 16 + d * ES));
+          const uint32_t hi = *reinterpret_cast<const uint16_t*>(vt + ((size_t)(t + 1) * PITCH * 16 + d * ES));
+          w[e] = lo | (hi << 16);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          w[e] = *reinterpret_cast<const uint32_t*>(vt + ((size_t)(X * q + e) * PITCH * 16 + d * ES));
+      }
+      vdst[idx] = u32x4{w[0], w[1], w[2], w[3]};
+    }
+    return;
   }
 
   // V: element d of token t -> v_pool[blk, g, d, off]

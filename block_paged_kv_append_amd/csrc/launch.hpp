@@ -131,6 +131,10 @@ struct CheckArgs {
 };
 
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
+// a plain read of bytes (a multiple of 16) at buf by num_wgs workgroups;
+// out [num_wgs] receives one folded word each
+hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* out, int num_wgs,
+                           hipStream_t stream);
 hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);

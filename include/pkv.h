@@ -456,6 +456,19 @@ int paged_attn_mixed(void* out, float* lse, const void* q, const int32_t* cu_q_l
                      void* workspace, size_t workspace_bytes, int32_t dtype,
                      struct ihipStream_t* stream);
 
+/*
+ * pkv_hbm_read_probe -- a measurement aid, not part of the attention path: a
+ * plain read of `bytes` (a multiple of 16) at device pointer `buf` by
+ * `num_wgs` workgroups of 256 lanes (16-byte loads, four in flight per lane),
+ * each writing one folded word to device array out [num_wgs].  Timed around
+ * a buffer larger than the 256 MB Infinity Cache, it gives the HBM read rate
+ * a kernel reaches on this GPU, the practical ceiling of the bandwidth-bound
+ * decode (which the page "Inference Server", section "The engine", runs
+ * over the block-paged cache every tick).  bytes == 0 is a no-op.
+ */
+int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* out, int32_t num_wgs,
+                       struct ihipStream_t* stream);
+
 /* Message describing the calling thread's last failed call ("" if none). */
 const char* pkv_last_error(void);
 

@@ -112,3 +112,19 @@ def test_large_slot_mapping_and_tables():
 def test_empty_check_reports_nothing():
     assert pkv.check_paged_metadata(4) == 0
     torch.cuda.synchronize()
+
+
+def test_hbm_read_probe_reads_every_word_once():
+    """The read probe folds every 32-bit word of the buffer into the
+    workgroups' words by XOR: their XOR is the XOR of the whole buffer (each
+    word read exactly once), for sizes with and without a ragged tail."""
+    for nbytes, wgs in ((1 << 20, 64), (3 * 4096 + 48, 7), (16, 1)):
+        print("\n[case] read probe", nbytes, wgs, flush=True)
+        host = np.random.default_rng(nbytes).integers(0, 2**32, size=nbytes // 4, dtype=np.uint64)
+        host = host.astype(np.uint32)
+        buf = torch.from_numpy(host.view(np.int32).copy()).cuda()
+        out = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+        pkv.hbm_read_probe(buf, out, num_wgs=wgs)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+        assert got == np.bitwise_xor.reduce(host)
