@@ -53,11 +53,29 @@ namespace {
 // counts the segment's last piece then reads every partial with device-scope
 // loads.  No cache writeback or invalidation is needed (a release/acquire
 // fence pair would write back and invalidate a whole L2 per piece).
-__device__ __forceinline__ void store_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ float load_dev(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Device-scope stores of 16 and 8 bytes through a buffer resource over a
+// region uniform in the workgroup: write-through (sc1) stores, the
+// instruction a relaxed agent-scope atomic store of one float compiles to,
+// one instruction instead of four.  The merge reads partials the same way,
+// 16 bytes per load through a resource over the whole partials region (when
+// it spans less than 2 GiB; else per float).
+constexpr int kDeviceScope = 16;  // cache policy: sc1
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t region(void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000u);
+}
+__device__ __forceinline__ void store_dev4(__amdgpu_buffer_rsrc_t r, int byte_off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, byte_off, 0, kDeviceScope);
+}
+__device__ __forceinline__ void store_dev2(__amdgpu_buffer_rsrc_t r, int byte_off, float x, float y) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(x), __float_as_uint(y)}, r, byte_off, 0,
+                                        kDeviceScope);
+}
+__device__ __forceinline__ f32x4 load_dev4(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kDeviceScope));
 }
 
 // Timeline build (PKV_TIMELINE): a workgroup's phases as s_memrealtime
@@ -248,6 +266,10 @@ __device__ void merge_segment(const DecodeArgs& a, int b, int g, SlotList slots,
   const int R = G * kLanes;      // (head, column) pairs
   const int groups = R >= kThreads ? 1 : kThreads / R;
   const int cnt = slots.count();
+  const long long nsl = a.part_blocks > 0 ? (long long)a.num_seqs * a.num_kv_heads * a.num_partitions
+                                          : 2LL * a.num_workers;
+  const bool wide = nsl * G * D * 4 < (1LL << 31);
+  const __amdgpu_buffer_rsrc_t ro = region(a.part_o, wide ? (int)(nsl * G * D * 4) : 0);
   for (int e0 = 0; e0 < R; e0 += kThreads) {
     const int e = groups > 1 ? (int)threadIdx.x % R : e0 + (int)threadIdx.x;
     const int grp = groups > 1 ? (int)threadIdx.x / R : 0;
@@ -270,7 +292,10 @@ __device__ void merge_segment(const DecodeArgs& a, int b, int g, SlotList slots,
           mk[q] = load_dev(a.part_ml + ((size_t)sl * G + h) * 2);
           lk[q] = load_dev(a.part_ml + ((size_t)sl * G + h) * 2 + 1);
           const float* po = a.part_o + ((size_t)sl * G + h) * D + 4 * col;
-          ov[q] = f32x4{load_dev(po), load_dev(po + 1), load_dev(po + 2), load_dev(po + 3)};
+          if (wide)
+            ov[q] = load_dev4(ro, (int)((((size_t)sl * G + h) * D + 4 * col) * 4));
+          else
+            ov[q] = f32x4{load_dev(po), load_dev(po + 1), load_dev(po + 2), load_dev(po + 3)};
         }
       }
       float Mn = M;
@@ -386,6 +411,9 @@ __device__ void combine_waves(const DecodeArgs& a, const Piece& pc, const float*
   const SeqSpan& sp = pc.sp;
   const bool whole = (pc.j0 == 0 && pc.j1 == sp.nb);
   const int nvec = G * D / 4;
+  // the piece's partial: O [G][D] and (max, sum) [G][2] at its slot
+  const __amdgpu_buffer_rsrc_t ro = region(a.part_o + (size_t)pc.slot * G * D, G * D * 4);
+  const __amdgpu_buffer_rsrc_t rml = region(a.part_ml + (size_t)pc.slot * G * 2, G * 8);
   for (int e = threadIdx.x; e < nvec; e += kThreads) {
     const int h = (e * 4) / D, d = (e * 4) % D;
     float M = kNegInf;
@@ -404,15 +432,8 @@ __device__ void combine_waves(const DecodeArgs& a, const Piece& pc, const float*
     if (whole) {
       finalize_vec<BF16, D>(a, b, g * G + h, d, O, L, M);
     } else {
-      float* po = a.part_o + ((size_t)pc.slot * G + h) * D + d;
-      store_dev(po, O.x);
-      store_dev(po + 1, O.y);
-      store_dev(po + 2, O.z);
-      store_dev(po + 3, O.w);
-      if (d == 0) {
-        store_dev(a.part_ml + ((size_t)pc.slot * G + h) * 2, M);
-        store_dev(a.part_ml + ((size_t)pc.slot * G + h) * 2 + 1, L);
-      }
+      store_dev4(ro, (h * D + d) * 4, O);
+      if (d == 0) store_dev2(rml, h * 8, M, L);
     }
   }
 
@@ -766,9 +787,7 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
   char* ring = reinterpret_cast<char*>(lds) + wave * kRingBytesPerWave<D>;
-  // this wave's table entries, 64 at a time (lane l: block tbase + l); loaded
-  // before the fused append's set-up, whose own table read and branch would
-  // otherwise hold this load back
+  // this wave's table entries, 64 at a time (lane l: block tbase + l)
   int tbase = 0;
   int tbl = lane < nw ? tbl_at(lane) : 0;
   NewToken<2, D> nt;
