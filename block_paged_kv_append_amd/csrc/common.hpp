@@ -132,6 +132,7 @@ __device__ __forceinline__ long long wave_incl_scan_i64(long long v, int lane) {
 // blocks it touches, first_blk .. first_blk + nb - 1.
 // ---------------------------------------------------------------------------
 struct SeqSpan {
+  int L_raw;      // context length as given
   int L;          // context length, clamped to [0, max_len]
   int vis_lo;     // first visible token (window), 0 without a window
   int first_blk;  // logical block holding vis_lo
@@ -141,6 +142,7 @@ struct SeqSpan {
 // max_len: the largest length the caller promised (and the block table can hold)
 __device__ __forceinline__ SeqSpan seq_span(int L_raw, int window, int max_len) {
   SeqSpan s;
+  s.L_raw = L_raw;
   s.L = min(max(L_raw, 0), max_len);
   s.vis_lo = (window > 0) ? max(0, s.L - window) : 0;
   s.first_blk = s.vis_lo / kBlock;

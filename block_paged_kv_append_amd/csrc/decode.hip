@@ -140,16 +140,18 @@ struct NewToken {
   char* kt = nullptr;  // the block's K and V tiles (kv head g) in the pool
   char* vt = nullptr;
 
-  // wave `wave` walks blocks j0 + wave + 4 i, i < nw, of the piece [j0, j1)
+  // wave `wave` walks blocks j0 + wave + 4 i, i < nw, of the piece [j0, j1);
+  // tbl holds the wave's first table entries (lane i: its block i)
   __device__ __forceinline__ void setup(const DecodeArgs& a, int b, int g, const SeqSpan& sp, int j0,
-                                        int j1, int wave, int nw, int lane) {
+                                        int j1, int wave, int nw, int lane, int tbl) {
     const int last = sp.nb - 1;
     own = j1 == sp.nb && nw > 0 && j0 + wave + kWaves * (nw - 1) == last;
     if (!own) return;
-    const int phys = a.block_tables[(size_t)b * a.max_blocks_per_seq + sp.first_blk + last];
+    const int phys = nw <= kWave ? __builtin_amdgcn_readlane(tbl, nw - 1)
+                                 : a.block_tables[(size_t)b * a.max_blocks_per_seq + sp.first_blk + last];
     // an unreadable block, or a length beyond max_context_len (its clamped
     // last position holds an older token): nothing to write
-    if ((unsigned)phys >= (unsigned)a.num_blocks || a.context_lens[b] > a.max_context_len) {
+    if ((unsigned)phys >= (unsigned)a.num_blocks || sp.L_raw > a.max_context_len) {
       own = false;
       return;
     }
@@ -489,7 +491,11 @@ __device__ void run_piece(const DecodeArgs& a, const LogitXform& xf, const Piece
   const int nw = span > 0 ? (span + kWaves - 1) / kWaves : 0;
   int tbl = 0;
   NewToken<sizeof(T), D> nt;
-  if constexpr (FUSE) nt.setup(a, b, g, sp, pc.j0, pc.j1, wave, nw, lane);
+  if constexpr (FUSE) {
+    const int t0 = nw > 0 ? a.block_tables[(size_t)b * a.max_blocks_per_seq + sp.first_blk + pc.j0 + wave +
+                                           kWaves * min(lane, nw - 1)] : 0;
+    nt.setup(a, b, g, sp, pc.j0, pc.j1, wave, nw, lane, t0);
+  }
 
   // One K and one V register set.  K of block i + 1 is loaded as soon as the
   // score product of block i has consumed K, V of block i + 1 as soon as the
@@ -759,6 +765,7 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   sp.nb = __builtin_amdgcn_readfirstlane(pc.sp.nb);
   sp.vis_lo = __builtin_amdgcn_readfirstlane(pc.sp.vis_lo);
   sp.L = __builtin_amdgcn_readfirstlane(pc.sp.L);
+  sp.L_raw = __builtin_amdgcn_readfirstlane(pc.sp.L_raw);
   const SinkPart sk = EVICT ? sink_part(sp, a.window, a.sink) : SinkPart{0, 0};
 
   // query fragments: every lane loads from a real row (columns past the
@@ -791,7 +798,7 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
   int tbase = 0;
   int tbl = lane < nw ? tbl_at(lane) : 0;
   NewToken<2, D> nt;
-  if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
+  if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane, tbl);
   uint32_t okbits = 0;  // bit (block % NS): that slot's block was readable
 #ifdef PKV_TIMELINE
   if (pc.ord == 0) {
@@ -942,6 +949,7 @@ __device__ void run_piece_stream(const DecodeArgs& a, const LogitXform& xf, cons
   sp.nb = __builtin_amdgcn_readfirstlane(pc.sp.nb);
   sp.vis_lo = __builtin_amdgcn_readfirstlane(pc.sp.vis_lo);
   sp.L = __builtin_amdgcn_readfirstlane(pc.sp.L);
+  sp.L_raw = __builtin_amdgcn_readfirstlane(pc.sp.L_raw);
   const int span = j1 - j0 - wave;
   const int nw = span > 0 ? (span + kWaves - 1) / kWaves : 0;
 
@@ -987,7 +995,7 @@ __device__ void run_piece_stream(const DecodeArgs& a, const LogitXform& xf, cons
       rs.qn[s] = *reinterpret_cast<const u32x4*>(qrow + 32 * s) & (c < G ? 0xFFFFFFFFu : 0u);
   }
   NewToken<2, D> nt;
-  if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane);
+  if constexpr (FUSE) nt.setup(a, b, g, sp, j0, j1, wave, nw, lane, tbl);
 
   f32x4 o[XT];
 #pragma unroll
