@@ -60,6 +60,8 @@ def parse_args():
                    help="run only a plain device copy of known size (HBM counter calibration)")
     p.add_argument("--timeline-raw", metavar="FILE.npy", default=None,
                    help="with --timeline: also save the raw stamps of the live workgroups")
+    p.add_argument("--copy-only", action="store_true",
+                   help="only the copy-on-write block copy timing (for counter runs)")
     p.add_argument("--decode-only", metavar="WORKLOAD", default=None,
                    choices=["gemma_decode", "sliding_window_decode", "long_context_splitk"],
                    help="only the decode timing of WORKLOAD (for counter runs)")
@@ -708,6 +710,13 @@ def main():
     if args.timeline:
         print(json.dumps(timeline(args.timeline, torch, pkv, wl, raw_out=args.timeline_raw)),
               flush=True)
+        return
+    if args.copy_only:
+        c = wl.gemma_decode()
+        b = DecodeBench(c, 0, torch, pkv)
+        ms, pairs, nbytes = time_copy_blocks(b, 20, torch)
+        print(json.dumps({"copy_blocks_pairs": pairs, "ms": round(ms, 5),
+                          "gbs": round(nbytes / (ms * 1e-3) / 1e9, 1), "bytes": nbytes}))
         return
     if args.decode_only:
         c = getattr(wl, args.decode_only)()
