@@ -23,11 +23,11 @@
 namespace pkv {
 namespace {
 
-template <int D, bool SC>
+template <int D, bool SC, bool FLAT>
 __global__ __launch_bounds__(kThreads, 1) void mixed_kernel(PrefillArgs pa, DecodeArgs da) {
   extern __shared__ float lds[];
   if ((int)blockIdx.x < pa.num_items)
-    prefill_mma32_body<D, PKV_PREFILL_RING, SC>(pa, blockIdx.x, reinterpret_cast<u32x4*>(lds));
+    prefill_mma32_body<D, PKV_PREFILL_RING, SC, FLAT>(pa, blockIdx.x, reinterpret_cast<u32x4*>(lds));
   else
     decode_body<true, D, false, false, false>(da, blockIdx.x - pa.num_items, lds);
 }
@@ -53,7 +53,9 @@ hipError_t launch_m(const PrefillArgs& pa, DecodeArgs da, hipStream_t stream) {
   lds = std::max(lds, (size_t)kWaves * kRingBytesPerWave<D>);
   const long long grid = (long long)pa.num_items + da.num_workers;
   if (grid > INT_MAX) return hipErrorInvalidValue;
-  auto kernel = pa.softcap > 0.f ? mixed_kernel<D, true> : mixed_kernel<D, false>;
+  const bool flat = prefill_flat<D>(pa);
+  auto kernel = pa.softcap > 0.f ? (flat ? mixed_kernel<D, true, true> : mixed_kernel<D, true, false>)
+                                 : (flat ? mixed_kernel<D, false, true> : mixed_kernel<D, false, false>);
   hipError_t e = allow_lds(kernel, lds);
   if (e != hipSuccess) return e;
   kernel<<<(unsigned)grid, kThreads, lds, stream>>>(pa, da);

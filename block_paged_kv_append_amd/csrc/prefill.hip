@@ -260,8 +260,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* base, in
 // 16 bytes per lane from the buffer into LDS; a wave writes 1 KiB starting at
 // wave_dst, lane i at +16 i.  A buffer (not global) copy: the compiler's LDS
 // wait counting stays exact around it.
-__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int byte_off, u32x4* wave_dst) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)wave_dst, 16, byte_off, 0, 0, 0);
+__device__ __forceinline__ void copy_to_lds(__amdgpu_buffer_rsrc_t r, int byte_off, uint32_t sbyte_off,
+                                            u32x4* wave_dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)wave_dst, 16, byte_off,
+                                           (int)sbyte_off, 0, 0);
 }
 
 // LDS of the matrix-core prefill: NB stages of K and V runs
@@ -274,7 +276,7 @@ constexpr size_t kPrefillLdsBytes = (size_t)NB * kPrefillStageU4<D, NB> * 16;
 // `smem` its stage ring in LDS.  prefill_mma32_kernel runs it for its own
 // workgroup; the mixed-batch kernel runs it for the first workgroups of its
 // grid.
-template <int D, int NB, bool SC>
+template <int D, int NB, bool SC, bool FLAT>
 __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk, u32x4* smem) {
   constexpr int KD = D / 16;                    // K runs per stage = QK products
   constexpr int XT = D / 32;                    // output row tiles of O^T
@@ -380,8 +382,18 @@ __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk
   uint32_t tailbits = 0;  // bit stage % NB: some key of the stage is past the context or unreadable
   // Copies of one stage: descriptors made once (prepare), the copies issued
   // one every second product of the next P V phase (copy); in one burst
-  // they would hold the waves on the vector memory path.
+  // they would hold the waves on the vector memory path.  A wave copies the
+  // runs of one block of the stage, block (wave & 1).  FLAT (each pool under
+  // 4 GiB): one descriptor per pool for the whole call, and per stage only
+  // the byte offset of the wave's block (an unreadable block reads block 0,
+  // whose keys are masked and whose values are cleared like a tail's);
+  // otherwise a descriptor per block, empty for an unreadable one.
   __amdgpu_buffer_rsrc_t crk0, crk1, crv0, crv1;
+  uint32_t csoff = 0;
+  const __amdgpu_buffer_rsrc_t rkp =
+      tile_rsrc(kpool, FLAT ? (int)(uint32_t)((size_t)a.num_blocks * Hkv * kTileU4 * 16) : 0);
+  const __amdgpu_buffer_rsrc_t rvp =
+      tile_rsrc(vpool, FLAT ? (int)(uint32_t)((size_t)a.num_blocks * Hkv * kTileU4 * 16) : 0);
   u32x4* cdst = smem;
   auto prepare = [&](int st) {
     if (2 * st - tbl_base >= 64) {  // uniform, every 32 stages
@@ -397,17 +409,24 @@ __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk
       const int lb = 2 * st + q;
       const bool ok = lb < nblk && (unsigned)cur[q] < (unsigned)a.num_blocks;
       ok2 |= (uint32_t)ok << q;
-      const size_t off = ((size_t)(ok ? cur[q] : 0) * Hkv + g) * kTileU4;
-      // an unreadable block gets an empty range: its copies read zeros
-      const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kpool + off, ok ? kTileU4 * 16 : 0);
-      const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vpool + off, ok ? kTileU4 * 16 : 0);
-      if (q == 0) {
-        crk0 = rk;
-        crv0 = rv;
-      } else {
-        crk1 = rk;
-        crv1 = rv;
+      if constexpr (!FLAT) {
+        const size_t off = ((size_t)(ok ? cur[q] : 0) * Hkv + g) * kTileU4;
+        // an unreadable block gets an empty range: its copies read zeros
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kpool + off, ok ? kTileU4 * 16 : 0);
+        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vpool + off, ok ? kTileU4 * 16 : 0);
+        if (q == 0) {
+          crk0 = rk;
+          crv0 = rv;
+        } else {
+          crk1 = rk;
+          crv1 = rv;
+        }
       }
+    }
+    if constexpr (FLAT) {
+      const int q = wave & 1;  // the block this wave copies
+      const int ph = q ? cur[1] : cur[0];
+      csoff = ((ok2 >> q) & 1u) ? (uint32_t)(ph * Hkv + g) * (uint32_t)(kTileU4 * 16) : 0u;
     }
     const int tok0 = (blk_lo + 2 * st) * kBlock;
     const bool full = ok2 == 3u && tok0 + 31 < L && tok0 + 31 <= qpos_lo &&
@@ -425,10 +444,18 @@ __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk
   auto copy = [&](int j) {
     if (j < KD / kWaves) {
       const int pr = 2 * j + (wave >> 1);
-      copy_to_lds((wave & 1) ? crk1 : crk0, (64 * pr + k_off) * 16, cdst + pr * 2 * kWave + (wave & 1) * kWave);
+      u32x4* dst = cdst + pr * 2 * kWave + (wave & 1) * kWave;
+      if constexpr (FLAT)
+        copy_to_lds(rkp, (64 * pr + k_off) * 16, csoff, dst);
+      else
+        copy_to_lds((wave & 1) ? crk1 : crk0, (64 * pr + k_off) * 16, 0, dst);
     } else {
       const int x = 2 * (j - KD / kWaves) + (wave >> 1);
-      copy_to_lds((wave & 1) ? crv1 : crv0, (64 * x + v_off) * 16, cdst + (KD + 2 * x + (wave & 1)) * kWave);
+      u32x4* dst = cdst + (KD + 2 * x + (wave & 1)) * kWave;
+      if constexpr (FLAT)
+        copy_to_lds(rvp, (64 * x + v_off) * 16, csoff, dst);
+      else
+        copy_to_lds((wave & 1) ? crv1 : crv0, (64 * x + v_off) * 16, 0, dst);
     }
   };
   auto issue = [&](int st) {
@@ -630,18 +657,32 @@ __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk
                 pack_bf16x2_hw(o[x][4 * h + 2] * inv, o[x][4 * h + 3] * inv)};
 }
 
-template <int D, int NB, bool SC>
+template <int D, int NB, bool SC, bool FLAT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs a) {
   __shared__ u32x4 smem[NB * kPrefillStageU4<D, NB>];
-  prefill_mma32_body<D, NB, SC>(a, blockIdx.x, smem);
+  prefill_mma32_body<D, NB, SC, FLAT>(a, blockIdx.x, smem);
+}
+
+// each pool addressable by one buffer descriptor (32-bit offsets)
+template <int D>
+bool prefill_flat(const PrefillArgs& a) {
+  return (unsigned long long)a.num_blocks * a.num_kv_heads * D * kBlock * 2 <= 0xFFFFFFFFull;
 }
 
 template <int D>
 void launch_mma32(PrefillArgs a, hipStream_t stream) {
-  if (a.softcap > 0.f)
-    prefill_mma32_kernel<D, PKV_PREFILL_RING, true><<<a.num_items, kThreads, 0, stream>>>(a);
-  else
-    prefill_mma32_kernel<D, PKV_PREFILL_RING, false><<<a.num_items, kThreads, 0, stream>>>(a);
+  const bool flat = prefill_flat<D>(a);
+  if (a.softcap > 0.f) {
+    if (flat)
+      prefill_mma32_kernel<D, PKV_PREFILL_RING, true, true><<<a.num_items, kThreads, 0, stream>>>(a);
+    else
+      prefill_mma32_kernel<D, PKV_PREFILL_RING, true, false><<<a.num_items, kThreads, 0, stream>>>(a);
+  } else {
+    if (flat)
+      prefill_mma32_kernel<D, PKV_PREFILL_RING, false, true><<<a.num_items, kThreads, 0, stream>>>(a);
+    else
+      prefill_mma32_kernel<D, PKV_PREFILL_RING, false, false><<<a.num_items, kThreads, 0, stream>>>(a);
+  }
 }
 
 template <bool BF16, int D, int RT>
