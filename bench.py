@@ -512,6 +512,30 @@ def read_rate(torch, pkv) -> float:
     return n / (ms * 1e-3) / 1e9
 
 
+def gemm_rate(torch) -> float:
+    """TFLOP/s of a plain 8192^3 bf16 matrix product through torch (hipBLASLt)
+    on N(0, 1) operands: the matrix-core rate a tuned library GEMM reaches on
+    this GPU right now (the part is power-limited well below its listed
+    dense peak on random data), context for the prefill's rate."""
+    n = 8192
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    a = torch.randn(n, n, generator=g, device="cuda").to(torch.bfloat16)
+    b = torch.randn(n, n, generator=g, device="cuda").to(torch.bfloat16)
+    for _ in range(3):
+        c = a @ b
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        c = a @ b
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / 10
+    del a, b, c
+    torch.cuda.empty_cache()
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
 def calibrate_copy(torch):
     """A plain device-to-device copy of 1 GiB, 10 times: the reference for
     scaling the HBM FETCH_SIZE / WRITE_SIZE counters."""
@@ -840,6 +864,9 @@ def main():
         rr = read_rate(torch, pkv)
         line["box_read_gbs"] = round(rr, 1)
         line["roofline"]["frac_of_box_read"] = round(achieved / rr, 4)
+        gr = gemm_rate(torch)
+        line["box_gemm_tflops"] = round(gr, 1)
+        line["prefill"]["roofline"]["frac_of_box_gemm"] = round(line["prefill"]["tflops"] / gr, 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)
