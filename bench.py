@@ -65,6 +65,9 @@ def parse_args():
     p.add_argument("--decode-only", metavar="WORKLOAD", default=None,
                    choices=["gemma_decode", "sliding_window_decode", "long_context_splitk"],
                    help="only the decode timing of WORKLOAD (for counter runs)")
+    p.add_argument("--partition-size", type=int, default=None,
+                   help="with --decode-only: run the split-K decode with this partition size "
+                        "(0: the balanced split) instead of the workload's own")
     p.add_argument("--timeline", metavar="WORKLOAD", default=None,
                    choices=["gemma_decode", "sliding_window_decode"],
                    help="per-workgroup phase breakdown of one decode launch of WORKLOAD; needs "
@@ -744,9 +747,12 @@ def main():
         return
     if args.decode_only:
         c = getattr(wl, args.decode_only)()
+        if args.partition_size is not None:
+            c.partition_size = args.partition_size
         b = DecodeBench(c, 0, torch, pkv)
         ms = time_decode_op(b, 20, torch)
-        print(json.dumps({"decode_only": c.name, "ms": round(ms, 5),
+        print(json.dumps({"decode_only": c.name, "partition_size": c.partition_size,
+                          "ms": round(ms, 5),
                           "gbs": round(decode_bytes(c) / (ms * 1e-3) / 1e9, 1),
                           "algorithmic_bytes": decode_bytes(c), "pool_replicas": b.R}))
         return
