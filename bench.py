@@ -493,26 +493,55 @@ def copy_rate(torch) -> float:
     return 2 * n / (ms * 1e-3) / 1e9
 
 
-def read_rate(torch, pkv) -> float:
-    """GB/s of a plain read of 2 GiB (the library's read probe, 8 workgroups
-    per compute unit): the HBM read rate a kernel reaches on this GPU right
-    now, the practical ceiling of the decode."""
-    n = 2 << 30
-    buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(3)
-    out = torch.empty(8 * torch.cuda.get_device_properties(0).multi_processor_count,
-                      dtype=torch.int32, device="cuda")
-    for _ in range(3):
-        pkv.hbm_read_probe(buf, out)
+def _events_ms(torch, fn, reps=10, warm=3):
+    for _ in range(warm):
+        fn()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(10):
-        pkv.hbm_read_probe(buf, out)
+    for _ in range(reps):
+        fn()
     e1.record()
     torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / 10
+    return e0.elapsed_time(e1) / reps
+
+
+def read_rate(torch, pkv):
+    """GB/s of a plain sequential read of 2 GiB (the library's read probe),
+    the best over 2, 4, 8 and 16 workgroups per compute unit: the highest
+    HBM read rate a kernel reaches on this GPU right now.  Returns (best
+    GB/s, {workgroups per CU: GB/s})."""
+    n = 2 << 30
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    buf = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(3)
+    out = torch.empty(16 * cus, dtype=torch.int32, device="cuda")
+    rates = {}
+    for per_cu in (2, 4, 8, 16):
+        ms = _events_ms(torch, lambda: pkv.hbm_read_probe(buf, out, num_wgs=per_cu * cus))
+        rates[per_cu] = round(n / (ms * 1e-3) / 1e9, 1)
     del buf, out
     torch.cuda.empty_cache()
-    return n / (ms * 1e-3) / 1e9
+    return max(rates.values()), rates
+
+
+def gather_rate(torch, pkv, bench):
+    """GB/s of reading whole blocks of the decode bench's pools (K and V of
+    every block of every replica, 32 KiB per block) in a random order (the
+    library's gather probe, one and two workgroups per compute unit, the
+    better): the decode's access pattern without its arithmetic."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nb = bench.kp.shape[0]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(11)
+    order = torch.randperm(nb, generator=g, device="cuda").to(torch.int32)
+    out = torch.empty(2 * cus, dtype=torch.int32, device="cuda")
+    nbytes = 2 * bench.kp.numel() * bench.kp.element_size()
+    best = 0.0
+    for per_cu in (1, 2):
+        ms = _events_ms(torch, lambda: pkv.hbm_gather_probe(bench.kp, bench.vp, order, out,
+                                                          num_wgs=per_cu * cus))
+        best = max(best, nbytes / (ms * 1e-3) / 1e9)
+    del order, out
+    return best
 
 
 def gemm_rate(torch) -> float:
@@ -867,9 +896,13 @@ def main():
 
     if not args.quick:
         line["box_copy_gbs"] = round(copy_rate(torch), 1)
-        rr = read_rate(torch, pkv)
+        rr, rr_all = read_rate(torch, pkv)
         line["box_read_gbs"] = round(rr, 1)
+        line["box_read_gbs_by_wgs_per_cu"] = rr_all
         line["roofline"]["frac_of_box_read"] = round(achieved / rr, 4)
+        gbr = gather_rate(torch, pkv, bench)
+        line["box_block_gather_gbs"] = round(gbr, 1)
+        line["roofline"]["frac_of_box_block_gather"] = round(achieved / gbr, 4)
         gr = gemm_rate(torch)
         line["box_gemm_tflops"] = round(gr, 1)
         line["prefill"]["roofline"]["frac_of_box_gemm"] = round(line["prefill"]["tflops"] / gr, 4)

@@ -66,6 +66,7 @@ SIGNATURES = {
                                         _I, _I, _I, _I, _F, _F, _I, _P, _Z, _I, _P]),
     "pkv_check_paged_metadata": (ctypes.c_int, [_P, _P, _I, _I, _I, _P, _I, _P, _P]),
     "pkv_hbm_read_probe": (ctypes.c_int, [_P, _Z, _P, _I, _P]),
+    "pkv_hbm_gather_probe": (ctypes.c_int, [_P, _P, _Z, _I, _P, _I, _P, _I, _P]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
 
@@ -526,6 +527,27 @@ def hbm_read_probe(buf, out, num_wgs=None, stream=None) -> None:
     lib = load_library()
     _check("pkv_hbm_read_probe", lib.pkv_hbm_read_probe(_ptr(buf), buf.numel() * buf.element_size(),
                                                         _ptr(out), int(n), _stream(stream)))
+
+
+def hbm_gather_probe(k, v, order, out, num_wgs=None, stream=None) -> None:
+    """A read of whole blocks ``order`` (int32 device tensor of block ids) of
+    ``k`` and ``v`` (device tensors whose first dimension is the block, each
+    block a multiple of 4 KiB): the decode's access pattern over a shuffled
+    pool.  ``num_wgs`` workgroups (default: one per compute unit) each write
+    one word of ``out``."""
+    import torch
+
+    n = num_wgs or torch.cuda.get_device_properties(k.device).multi_processor_count
+    if out.numel() < n or out.element_size() != 4:
+        raise ValueError("out needs num_wgs 32-bit entries")
+    if k.shape[0] != v.shape[0] or k.numel() != v.numel() or k.dtype != v.dtype:
+        raise ValueError("k and v must have the same blocks, sizes and dtype")
+    nb = k.shape[0]
+    block_bytes = k.numel() * k.element_size() // nb
+    lib = load_library()
+    _check("pkv_hbm_gather_probe",
+           lib.pkv_hbm_gather_probe(_ptr(k), _ptr(v), block_bytes, nb, _i32(order, "order"),
+                                    order.numel(), _ptr(out), int(n), _stream(stream)))
 
 
 def from_bits(bits, dtype: str, device="cuda"):

@@ -383,6 +383,22 @@ int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* out, int32_t num
                                        reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+int pkv_hbm_gather_probe(const void* k, const void* v, size_t block_bytes, int32_t num_blocks,
+                         const int32_t* order, int32_t n, uint32_t* out, int32_t num_wgs,
+                         struct ihipStream_t* stream) {
+  const char* fn = "pkv_hbm_gather_probe";
+  if (n == 0) return PKV_OK;
+  if (!k || !v || !order || !out) return fail(PKV_EINVAL, "%s: null pointer", fn);
+  if (n < 0 || num_blocks < 1 || block_bytes == 0 || block_bytes % 4096 != 0 ||
+      block_bytes / 16 > (size_t)INT_MAX || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(order, 4) || !aligned(out, 4))
+    return fail(PKV_EINVAL, "%s: n %d, block_bytes %zu (a multiple of 4096), or misaligned", fn,
+                n, block_bytes);
+  if (num_wgs < 1 || num_wgs > (1 << 20)) return fail(PKV_EINVAL, "%s: num_wgs %d", fn, num_wgs);
+  return from_hip(pkv::launch_hbm_gather(k, v, block_bytes, num_blocks, order, n, out, num_wgs,
+                                         reinterpret_cast<hipStream_t>(stream)), fn);
+}
+
 int pkv_check_paged_metadata(const int32_t* block_tables, const int32_t* context_lens,
                              int32_t num_seqs, int32_t max_blocks_per_seq, int32_t num_blocks,
                              const int32_t* slot_mapping, int32_t num_slots, uint32_t* flags,

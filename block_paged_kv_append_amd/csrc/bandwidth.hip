@@ -41,7 +41,55 @@ __global__ __launch_bounds__(kReadThreads) void hbm_read_kernel(const u32x4* buf
   }
 }
 
+// A gather of whole blocks in a given order: block order[i] of two pools
+// (block_bytes each, a multiple of 4 KiB), the decode's access pattern (a
+// block's K tile and V tile, blocks scattered over the pool).  Workgroup w
+// takes entries [w n / N, (w + 1) n / N) of the order, two blocks in flight.
+__global__ __launch_bounds__(kReadThreads) void hbm_gather_kernel(const u32x4* k, const u32x4* v,
+                                                                  const int32_t* order, int n,
+                                                                  int num_blocks, int chunks,
+                                                                  uint32_t* out) {
+  const int N = gridDim.x, w = blockIdx.x;
+  const int i0 = (int)((long long)w * n / N), i1 = (int)((long long)(w + 1) * n / N);
+  // an entry outside the buffers reads block 0 instead
+  auto blk = [&](int i) -> size_t {
+    const int b = order[i];
+    return (size_t)((unsigned)b < (unsigned)num_blocks ? b : 0) * chunks;
+  };
+  auto fold = [](u32x4 x) { return x.x ^ x.y ^ x.z ^ x.w; };
+  uint32_t acc = 0;
+  for (int i = i0; i < i1; i += 2) {
+    const bool two = i + 1 < i1;  // the range's last entry may be alone
+    const size_t b0 = blk(i);
+    const size_t b1 = blk(two ? i + 1 : i);
+    for (int c = threadIdx.x; c < chunks; c += kReadThreads) {
+      const u32x4 x0 = __builtin_nontemporal_load(k + b0 + c), y0 = __builtin_nontemporal_load(v + b0 + c);
+      const u32x4 x1 = __builtin_nontemporal_load(k + b1 + c), y1 = __builtin_nontemporal_load(v + b1 + c);
+      acc ^= fold(x0) ^ fold(y0) ^ (two ? fold(x1) ^ fold(y1) : 0u);
+    }
+  }
+  for (int o = 32; o >= 1; o >>= 1) acc ^= __shfl_xor(acc, o);
+  __shared__ uint32_t part[kReadThreads / kWave];
+  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = acc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+    for (int q = 0; q < kReadThreads / kWave; ++q) r ^= part[q];
+    out[w] = r;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_hbm_gather(const void* k, const void* v, size_t block_bytes, int num_blocks,
+                             const int32_t* order, int n, uint32_t* out, int num_wgs,
+                             hipStream_t stream) {
+  if (n <= 0 || num_wgs <= 0) return hipSuccess;
+  hbm_gather_kernel<<<num_wgs, kReadThreads, 0, stream>>>(
+      reinterpret_cast<const u32x4*>(k), reinterpret_cast<const u32x4*>(v), order, n, num_blocks,
+      (int)(block_bytes / 16), out);
+  return hipGetLastError();
+}
 
 hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* out, int num_wgs,
                            hipStream_t stream) {

@@ -135,6 +135,11 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // out [num_wgs] receives one folded word each
 hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* out, int num_wgs,
                            hipStream_t stream);
+// a gather of whole blocks order[0..n) of two pools of num_blocks blocks
+// (block_bytes each, a multiple of 4096; entries outside read block 0)
+hipError_t launch_hbm_gather(const void* k, const void* v, size_t block_bytes, int num_blocks,
+                             const int32_t* order, int n, uint32_t* out, int num_wgs,
+                             hipStream_t stream);
 hipError_t launch_check(const CheckArgs& a, hipStream_t stream);
 hipError_t launch_copy_blocks(const CopyBlocksArgs& a, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, bool bf16, hipStream_t stream);

@@ -469,6 +469,20 @@ int paged_attn_mixed(void* out, float* lse, const void* q, const int32_t* cu_q_l
 int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* out, int32_t num_wgs,
                        struct ihipStream_t* stream);
 
+/*
+ * pkv_hbm_gather_probe -- a measurement aid beside pkv_hbm_read_probe: a read
+ * of whole blocks in a given order, block order[i] of each of two device
+ * buffers k and v (block_bytes each, a multiple of 4096), the access pattern
+ * of the decode over a shuffled block pool (a block's K tile and V tile,
+ * blocks scattered over the pool); num_blocks is the buffers' block count,
+ * and an order entry outside [0, num_blocks) reads block 0.  num_wgs workgroups of 256 lanes each take a contiguous
+ * range of the order, two blocks in flight, and write one folded word to
+ * out [num_wgs].  n == 0 is a no-op.
+ */
+int pkv_hbm_gather_probe(const void* k, const void* v, size_t block_bytes, int32_t num_blocks,
+                         const int32_t* order, int32_t n, uint32_t* out, int32_t num_wgs,
+                         struct ihipStream_t* stream);
+
 /* Message describing the calling thread's last failed call ("" if none). */
 const char* pkv_last_error(void);
 

@@ -128,3 +128,27 @@ def test_hbm_read_probe_reads_every_word_once():
         torch.cuda.synchronize()
         got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
         assert got == np.bitwise_xor.reduce(host)
+
+
+def test_hbm_gather_probe_reads_each_listed_block_once():
+    """The gather probe folds every 32-bit word of each listed block of K and V
+    into the workgroups' words by XOR (blocks listed twice cancel, entries
+    outside the pools read block 0); ragged ranges per workgroup."""
+    rng = np.random.default_rng(5)
+    nb, words = 37, 4096 // 4
+    k = rng.integers(0, 2**32, size=(nb, words), dtype=np.uint64).astype(np.uint32)
+    v = rng.integers(0, 2**32, size=(nb, words), dtype=np.uint64).astype(np.uint32)
+    order = rng.integers(0, nb, size=101).astype(np.int32)
+    order[[3, 50]] = [nb + 5, -2]  # outside the pools: block 0
+    kd = torch.from_numpy(k.view(np.int32).copy()).cuda()
+    vd = torch.from_numpy(v.view(np.int32).copy()).cuda()
+    for wgs in (1, 7, 64):
+        print("\n[case] gather probe", wgs, flush=True)
+        out = torch.zeros(wgs, dtype=torch.int32, device="cuda")
+        pkv.hbm_gather_probe(kd, vd, torch.from_numpy(order).cuda(), out, num_wgs=wgs)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(out.cpu().numpy().view(np.uint32))
+        ids = np.where((order >= 0) & (order < nb), order, 0)
+        want = np.bitwise_xor.reduce(np.bitwise_xor.reduce(k[ids], axis=1) ^
+                                     np.bitwise_xor.reduce(v[ids], axis=1))
+        assert got == want
