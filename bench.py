@@ -39,7 +39,7 @@ METRIC = "paged-decode KV GB/s (% HBM peak) + tok/s; paged-prefill TFLOP/s at 1 
 PROFILES = os.path.join(ROOT, "profiles")
 # what a kernel's HBM counters depend on: its sources and its argument struct
 KERNEL_SOURCES = {
-    "decode": (["decode.hip", "attn_tile.hpp", "common.hpp"], "DecodeArgs"),
+    "decode": (["decode.hip", "slots.hpp", "attn_tile.hpp", "common.hpp"], "DecodeArgs"),
     "prefill": (["prefill.hip", "attn_tile.hpp", "common.hpp"], "PrefillArgs"),
 }
 

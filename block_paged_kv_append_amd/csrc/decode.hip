@@ -40,6 +40,7 @@
 
 #include "attn_tile.hpp"
 #include "launch.hpp"
+#include "slots.hpp"
 
 namespace pkv {
 namespace {
@@ -346,66 +347,9 @@ __device__ void merge_segment(const DecodeArgs& a, int b, int g, SlotList slots,
   }
 }
 
-struct SplitSlots {  // fixed partitions p_lo .. p_hi of one segment
-  int base, p_lo, p_hi;
-  __device__ int count() const { return p_hi - p_lo + 1; }
-  __device__ bool slot(int k, int& s) const {
-    s = base + p_lo + k;
-    return true;
-  }
-};
-
-// Workgroups whose ranges meet the real units [S, E) of a segment, in the
-// split's coordinates (real units plus kPieceCost<D> cost units in front of
-// every segment, see decode_kernel); Sv = S - kPieceCost<D> is where the
-// segment's cost units start.  With W > N every range holds at least one
-// unit, so they are w_first .. w_last.  With W <= N a range holds one unit or
-// none, and the workgroups with an empty range (which store nothing and never
-// count in) lie between those; the pieces are then the owners of units S ..
-// E - 1, one each.  A workgroup whose range starts at or after Sv met the
-// segment first (slot 2 w), otherwise second (slot 2 w + 1).
-struct BalancedSlots {
-  long long W, S, E, Sv;
-  int N, w_first, w_last;
-  __device__ BalancedSlots(long long W_, long long S_, long long E_, long long Sv_, int N_)
-      : W(W_), S(S_), E(E_), Sv(Sv_), N(N_) {
-    w_first = (int)(((S + 1) * N - 1) / W);
-    w_last = (int)((E * N - 1) / W);
-  }
-  __device__ int count() const { return W <= N ? (int)(E - S) : w_last - w_first + 1; }
-  __device__ bool slot(int k, int& s) const {
-    const int w = W <= N ? (int)(((S + k + 1) * N - 1) / W) : w_first + k;
-    const long long a0 = (long long)w * W / N;
-    s = a0 < Sv ? 2 * w + 1 : 2 * w;
-    return true;
-  }
-};
-
 // The four waves' (max, sum, output) of one piece, in LDS as lo[wave][head][D]
 // and lml[wave][head][2]: merged, then written as the output (whole segment)
 // or as the piece's partial.
-// Pieces of the persistent split-K decode within one segment's items
-// [S, E) (of I items split over N workgroups): the workgroups whose item
-// ranges meet [S, E), each storing one partial at the slot of its first
-// partition in the segment (base + its first item - S).  With I <= N a range
-// holds one item or none, and the pieces are the owners of items S .. E - 1.
-struct RunSlots {
-  long long I, S, E;
-  int N, base, w_first, w_last;
-  __device__ RunSlots(long long I_, long long S_, long long E_, int N_, int base_)
-      : I(I_), S(S_), E(E_), N(N_), base(base_) {
-    w_first = (int)(((S + 1) * N - 1) / I);
-    w_last = (int)((E * N - 1) / I);
-  }
-  __device__ int count() const { return I <= N ? (int)(E - S) : w_last - w_first + 1; }
-  __device__ bool slot(int k, int& s) const {
-    const int w = I <= N ? (int)(((S + k + 1) * N - 1) / I) : w_first + k;
-    const long long first = max(S, (long long)w * I / N);
-    s = base + (int)(first - S);
-    return true;
-  }
-};
-
 template <bool BF16, int D, bool V = false>
 __device__ void combine_waves(const DecodeArgs& a, const Piece& pc, const float* lo, const float* lml) {
   const int G = a.gqa_group;
