@@ -28,6 +28,8 @@
 namespace pkv {
 namespace {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 
 template <bool BF16, int D, int RT>
 __global__ __launch_bounds__(kThreads, 1) void prefill_kernel(PrefillArgs a) {
@@ -663,6 +665,404 @@ __global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs 
   prefill_mma32_body<D, NB, SC, FLAT>(a, blockIdx.x, smem);
 }
 
+// ---------------------------------------------------------------------------
+// Two waves per SIMD ("ping-pong").  With one wave per SIMD, the vector work
+// of a stage (softmax, masking, addressing) issues mostly outside the
+// matrix-core products' shadow: a single wave hides only about two vector
+// instructions under each 32x32x16 product.  Here a workgroup has eight
+// waves; waves w and w + 4 share a SIMD and the same 32 query rows, and take
+// alternate stages (w < 4 the even ones, w >= 4 the odd ones), each with its
+// own online softmax over its stages.  While one wave of a pair is in its
+// softmax, the other's products keep the matrix core busy.  Each wave runs a
+// stage in order (S^T, softmax, P V), so no second score tile is live, and
+// the pair's two partial results are merged by log-sum-exp through LDS at
+// the end, each wave writing half of the output dims.
+//
+// Stages move through the same NB-slot LDS ring as above, one "interval"
+// (two stages, one per half) per barrier: at the barrier of interval i,
+// stages 2i and 2i + 1 have landed and every wave has finished interval
+// i - 1, so the copies of interval i + NB/2 - 1 go into the slots interval
+// i - 1 used.  Each half copies its own parity's stages, split over its four
+// waves exactly as in the four-wave form.
+template <int D, int NB>
+constexpr size_t kPrefillPPLdsBytes =
+    (size_t)NB * kPrefillStageU4<D, NB> * 16 > (size_t)8 * ((D / 64) * 16 * kWave + 2 * kWave) * 4
+        ? (size_t)NB * kPrefillStageU4<D, NB> * 16
+        : (size_t)8 * ((D / 64) * 16 * kWave + 2 * kWave) * 4;
+
+template <int D, int NB, bool SC, bool FLAT>
+__device__ __forceinline__ void prefill_pp_body(const PrefillArgs& a, int blk, u32x4* smem) {
+  constexpr int KD = D / 16;                    // K runs per stage = QK products
+  constexpr int XT = D / 32;                    // output row tiles of O^T
+  constexpr int kRuns = KD + 2 * XT;            // 1 KiB runs per stage
+  constexpr int kStageU4 = kRuns * kWave;       // 16-byte chunks per stage
+  constexpr int kDma = kRuns / kWaves;          // copies per wave per interval
+  constexpr int kAhead = D >= 256 ? 2 : 4;      // LDS operand reads in flight (registers)
+  constexpr int kTileU4 = D * kBlock * 2 / 16;  // chunks of one block's K (or V) in the pool
+  constexpr int kAheadIv = NB / 2 - 1;          // intervals the copies run ahead
+  static_assert(KD == 2 * kDma, "one copy every second S^T product");
+  static_assert(NB >= 4 && (NB & (NB - 1)) == 0, "ring of 4 or 8 stages");
+  static_assert(XT % 2 == 0, "output tiles split between the pair");
+
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wave = w & 3;  // row group (and copy share within a half)
+  const int half = w >> 2; // stage parity
+  const int n = lane & 31, kg = lane >> 5;
+  const int G = a.gqa_group, Hkv = a.num_kv_heads, Hq = G * Hkv;
+  const int PPW = 32 / G;
+  const LogitXform xf = make_xform(a.scale, a.softcap);
+  const bool flip_q = !SC && xf.scale_log2 < 0.f;
+  const float pos_scale_log2 = fmaxf(fabsf(xf.scale_log2), 1e-30f);
+
+  int item = blk;
+  if (a.num_items % 8 == 0) item = (int)((unsigned)blk % 8u) * (a.num_items / 8) + (int)((unsigned)blk / 8u);
+  const int tile = item % a.tiles_per_seq;
+  const int bg = item / a.tiles_per_seq;
+  const int g = bg % Hkv, b = bg / Hkv;
+
+  const int L = min(max(a.context_lens[b], 0), a.max_blocks_per_seq * kBlock);
+  const int r0 = min(max(a.cu_q_lens[b], 0), a.num_q_tokens);
+  const int r1 = min(max(a.cu_q_lens[b + 1], r0), a.num_q_tokens);
+  const int nq = r1 - r0;
+  const int pos_wg = tile * (kWaves * PPW);
+  if (pos_wg >= nq) return;  // whole workgroup, before any barrier
+  const int shift = L - nq;
+  const int pos_wave = pos_wg + wave * PPW;
+  const bool wave_live = pos_wave < nq;
+  const int pos = pos_wave + n / G;
+  const bool rvalid = pos < nq;
+  const int qpos = shift + pos;
+  const int head = g * G + n % G;
+  const int qpos_lo = shift + pos_wave;
+  const int qpos_hi = shift + min(pos_wave + PPW - 1, nq - 1);
+
+  const int p_hi = min(nq - 1, pos_wg + kWaves * PPW - 1);
+  const int last_tok = min(shift + p_hi, L - 1);
+  if (last_tok < 0) {
+    // every row of the workgroup sits before the cache: out = 0, lse = -inf
+    if (half == 0 && wave_live && rvalid) {
+      const size_t row = (size_t)(r0 + pos) * Hq + head;
+      if (a.lse != nullptr && kg == 0) a.lse[row] = kNegInf;
+      uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + row * D + 4 * kg;
+#pragma unroll
+      for (int x = 0; x < D / 8; ++x) *reinterpret_cast<u32x2*>(dst + 8 * x) = u32x2{0u, 0u};
+    }
+    return;
+  }
+
+  u32x4 qf[KD];
+  {
+    const uint16_t* row =
+        reinterpret_cast<const uint16_t*>(a.q) + ((size_t)(r0 + min(pos, nq - 1)) * Hq + head) * D + 8 * kg;
+#pragma unroll
+    for (int i = 0; i < KD; ++i) qf[i] = *reinterpret_cast<const u32x4*>(row + 16 * i);
+    if (flip_q) {
+      const uint32_t sgn = 0x80008000u;
+#pragma unroll
+      for (int i = 0; i < KD; ++i) qf[i] ^= u32x4{sgn, sgn, sgn, sgn};
+    }
+    // the query fragments stay in vector registers: with two waves per SIMD
+    // a wave has 256 registers, and using the accumulator file at all would
+    // split them evenly between the two files
+  }
+
+  const int first_tok = a.window > 0 ? max(0, shift + pos_wg - a.window + 1) : 0;
+  const int blk_lo = first_tok / kBlock;
+  const int nblk = last_tok / kBlock - blk_lo + 1;
+  const int nstage = (nblk + 1) / 2;
+  const int n_iv = (nstage + 1) / 2;
+  const int* bt = a.block_tables + (size_t)b * a.max_blocks_per_seq + blk_lo;
+  const u32x4* kpool = reinterpret_cast<const u32x4*>(a.k_pool);
+  const u32x4* vpool = reinterpret_cast<const u32x4*>(a.v_pool);
+
+  const int k_off = 16 * (lane >> 4) + ((lane & 3) | ((lane & 4) << 1) | ((lane & 8) >> 1));
+  const int v_off = 2 * n + kg;
+  const int k_rd = ((n >> 4) << 6) + (n & 15) + 16 * kg;
+
+  // block-table slices and per-slot stage flags, as in the four-wave form;
+  // a wave prepares (and later computes) only the stages of its parity
+  int tbl_cur = lane < nblk ? bt[lane] : 0;
+  int tbl_nxt = 64 + lane < nblk ? bt[64 + lane] : 0;
+  int tbl_base = 0;
+  uint32_t okbits = 0, fullbits = 0, tailbits = 0;
+  __amdgpu_buffer_rsrc_t crk0, crk1, crv0, crv1;
+  uint32_t csoff = 0;
+  const __amdgpu_buffer_rsrc_t rkp =
+      tile_rsrc(kpool, FLAT ? (int)(uint32_t)((size_t)a.num_blocks * Hkv * kTileU4 * 16) : 0);
+  const __amdgpu_buffer_rsrc_t rvp =
+      tile_rsrc(vpool, FLAT ? (int)(uint32_t)((size_t)a.num_blocks * Hkv * kTileU4 * 16) : 0);
+  u32x4* cdst = smem;
+  auto prepare = [&](int st) {
+    while (2 * st - tbl_base >= 64) {  // uniform
+      tbl_base += 64;
+      tbl_cur = tbl_nxt;
+      tbl_nxt = tbl_base + 64 + lane < nblk ? bt[tbl_base + 64 + lane] : 0;
+    }
+    const int cur[2] = {__builtin_amdgcn_readlane(tbl_cur, 2 * st - tbl_base),
+                        __builtin_amdgcn_readlane(tbl_cur, 2 * st + 1 - tbl_base)};
+    uint32_t ok2 = 0;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int lb = 2 * st + q;
+      const bool ok = lb < nblk && (unsigned)cur[q] < (unsigned)a.num_blocks;
+      ok2 |= (uint32_t)ok << q;
+      if constexpr (!FLAT) {
+        const size_t off = ((size_t)(ok ? cur[q] : 0) * Hkv + g) * kTileU4;
+        const __amdgpu_buffer_rsrc_t rk = tile_rsrc(kpool + off, ok ? kTileU4 * 16 : 0);
+        const __amdgpu_buffer_rsrc_t rv = tile_rsrc(vpool + off, ok ? kTileU4 * 16 : 0);
+        if (q == 0) {
+          crk0 = rk;
+          crv0 = rv;
+        } else {
+          crk1 = rk;
+          crv1 = rv;
+        }
+      }
+    }
+    if constexpr (FLAT) {
+      const int q = wave & 1;
+      const int ph = q ? cur[1] : cur[0];
+      csoff = ((ok2 >> q) & 1u) ? (uint32_t)(ph * Hkv + g) * (uint32_t)(kTileU4 * 16) : 0u;
+    }
+    const int tok0 = (blk_lo + 2 * st) * kBlock;
+    const bool full = ok2 == 3u && tok0 + 31 < L && tok0 + 31 <= qpos_lo &&
+                      (a.window <= 0 || qpos_hi - tok0 < a.window);
+    const bool tail = !(ok2 == 3u && tok0 + 2 * kBlock <= L);
+    const int slot = st & (NB - 1);
+    okbits = (okbits & ~(3u << (2 * slot))) | (ok2 << (2 * slot));
+    fullbits = (fullbits & ~(1u << slot)) | ((uint32_t)full << slot);
+    tailbits = (tailbits & ~(1u << slot)) | ((uint32_t)tail << slot);
+    cdst = smem + slot * kStageU4;
+  };
+  auto copy = [&](int j) {
+    if (j < KD / kWaves) {
+      const int pr = 2 * j + (wave >> 1);
+      u32x4* dst = cdst + pr * 2 * kWave + (wave & 1) * kWave;
+      if constexpr (FLAT)
+        copy_to_lds(rkp, (64 * pr + k_off) * 16, csoff, dst);
+      else
+        copy_to_lds((wave & 1) ? crk1 : crk0, (64 * pr + k_off) * 16, 0, dst);
+    } else {
+      const int x = 2 * (j - KD / kWaves) + (wave >> 1);
+      u32x4* dst = cdst + (KD + 2 * x + (wave & 1)) * kWave;
+      if constexpr (FLAT)
+        copy_to_lds(rvp, (64 * x + v_off) * 16, csoff, dst);
+      else
+        copy_to_lds((wave & 1) ? crv1 : crv0, (64 * x + v_off) * 16, 0, dst);
+    }
+  };
+
+  auto k_run = [](int s) { return (s >> 1) * 2 * kWave + (s & 1) * 32; };
+  auto stage_tok0 = [&](int st) { return (blk_lo + 2 * st) * kBlock; };
+  auto stage_ok = [&](int st) { return (okbits >> (2 * (st & (NB - 1)))) & 3u; };
+  auto stage_full = [&](int st) { return (fullbits >> (st & (NB - 1))) & 1u; };
+  auto stage_tail = [&](int st) { return (tailbits >> (st & (NB - 1))) & 1u; };
+
+  f32x16 o[XT];
+#pragma unroll
+  for (int x = 0; x < XT; ++x) o[x] = f32x16{};
+  float m_run = kNegInf, l_run = 0.f;
+  constexpr float kLazy = 8.0f;  // rescale only when the max grows by 2^8
+
+  // prologue: the copies of intervals 0 .. kAheadIv - 1
+  for (int iv = 0; iv < kAheadIv; ++iv) {
+    const int st = 2 * iv + half;
+    if (st < nstage) {
+      prepare(st);
+#pragma unroll
+      for (int j = 0; j < kDma; ++j) copy(j);
+    }
+  }
+
+  for (int iv = 0; iv < n_iv; ++iv) {
+    // this wave's copies of interval iv have landed (those of later intervals
+    // may still be in flight, unless there are none: the last intervals)
+    if constexpr (kAheadIv > 1) {
+      if (2 * (iv + kAheadIv - 1) + half < nstage)
+        wait_vmem<(kAheadIv - 1) * kDma>();
+      else
+        wait_vmem<0>();
+    } else {
+      wait_vmem<0>();
+    }
+    lds_barrier();  // ... and every other wave's; interval iv - 1 is done
+    const int st = 2 * iv + half;
+    const int st_copy = st + 2 * kAheadIv;
+    const bool do_copy = st_copy < nstage;
+    if (do_copy) prepare(st_copy);
+    if (!(wave_live && st < nstage)) {
+      if (do_copy) {
+#pragma unroll
+        for (int j = 0; j < kDma; ++j) copy(j);
+      }
+      continue;
+    }
+    const int slot = st & (NB - 1);
+
+    // S^T = K Q^T, with this interval's copies issued in its shadow
+    const u32x4* kb = smem + slot * kStageU4 + k_rd;
+    f32x16 acc = {};
+    {
+      u32x4 kf[kAhead];
+#pragma unroll
+      for (int i = 0; i < kAhead; ++i) kf[i] = kb[k_run(i)];
+#pragma unroll
+      for (int i = 0; i < KD; ++i) {
+        __builtin_amdgcn_sched_barrier(0);
+        acc = mma32_bf16(kf[i % kAhead], qf[i], acc);
+        if (i + kAhead < KD) kf[i % kAhead] = kb[k_run(i + kAhead)];
+        if ((i & 1) == 0 && do_copy) copy(i >> 1);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+
+    // keys past the context (or of an unreadable block): their V entries are
+    // cleared in LDS before the products read them (every wave computing this
+    // stage writes the same values)
+    if (stage_tail(st)) {
+      const int tok0 = stage_tok0(st);
+      const uint32_t okk = stage_ok(st);
+      u32x4* vr = smem + slot * kStageU4 + KD * kWave;
+      for (int c = lane; c < 2 * XT * kWave; c += kWave) {
+        const int q = (c >> 6) & 1, kgc = (c >> 5) & 1;
+        const int nv = ((okk >> q) & 1u) ? L - (tok0 + 16 * q) - 8 * kgc : 0;
+        if (nv >= 8) continue;
+        const u32x4 m = {(0 < nv ? 0x0000FFFFu : 0u) | (1 < nv ? 0xFFFF0000u : 0u),
+                         (2 < nv ? 0x0000FFFFu : 0u) | (3 < nv ? 0xFFFF0000u : 0u),
+                         (4 < nv ? 0x0000FFFFu : 0u) | (5 < nv ? 0xFFFF0000u : 0u),
+                         (6 < nv ? 0x0000FFFFu : 0u) | (7 < nv ? 0xFFFF0000u : 0u)};
+        vr[c] = vr[c] & m;
+      }
+      wait_lds();
+    }
+
+    mma_result_fence();
+    if (!stage_full(st)) {
+      const int tok0 = stage_tok0(st);
+      const uint32_t okk = stage_ok(st);
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int tk = tok0 + 16 * (v >> 3) + 8 * kg + (v & 7);
+        const bool vis = ((okk >> (v >> 3)) & 1u) & rvalid & (tk < L) & (tk <= qpos) &
+                         ((a.window <= 0) | (qpos - tk < a.window));
+        acc[v] = vis ? acc[v] : kNegInf;
+      }
+    }
+
+    // softmax of the stage: row max (base-2 logits), lazy rescale, then
+    // probabilities as bf16 pairs and their row sum
+    float mx = kNegInf;
+    if constexpr (SC) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float y = softcap_log2(acc[v] * xf.scale, xf.cap, xf.inv_cap);
+        acc[v] = acc[v] == kNegInf ? kNegInf : y;
+        mx = fmaxf(mx, acc[v]);
+      }
+      mx = half_max(mx);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, acc[v]);
+      mx = half_max(mx) * pos_scale_log2;
+    }
+    if (__any(mx > m_run + kLazy)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = fast_exp2(m_run - (m_new == kNegInf ? 0.f : m_new));
+      l_run *= alpha;
+#pragma unroll
+      for (int x = 0; x < XT; ++x) o[x] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == kNegInf ? 0.f : m_run;
+    uint32_t pw[8];
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) {
+      float p0, p1;
+      if constexpr (SC) {
+        p0 = fast_exp2(acc[v] - m_use);
+        p1 = fast_exp2(acc[v + 1] - m_use);
+      } else {
+        p0 = fast_exp2(fmaf(acc[v], pos_scale_log2, -m_use));
+        p1 = fast_exp2(fmaf(acc[v + 1], pos_scale_log2, -m_use));
+      }
+      pw[v >> 1] = pack_bf16x2_hw(p0, p1);
+      l_run += p0 + p1;
+    }
+    const u32x4 pb[2] = {u32x4{pw[0], pw[1], pw[2], pw[3]}, u32x4{pw[4], pw[5], pw[6], pw[7]}};
+
+    // O^T += V^T P^T
+    const u32x4* vb = smem + slot * kStageU4 + KD * kWave + lane;
+    {
+      constexpr int NU = 2 * XT;
+      u32x4 vf[kAhead];
+#pragma unroll
+      for (int u = 0; u < kAhead; ++u) vf[u] = vb[(2 * (u % XT) + u / XT) * kWave];
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        __builtin_amdgcn_sched_barrier(0);
+        const int x = u % XT, q = u / XT;
+        o[x] = mma32_bf16(vf[u % kAhead], pb[q], o[x]);
+        if (u + kAhead < NU) vf[u % kAhead] = vb[(2 * ((u + kAhead) % XT) + (u + kAhead) / XT) * kWave];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  wait_vmem<0>();  // no copy in flight: the ring is reused below
+  mma_result_fence();
+  lds_barrier();   // every wave is done with the ring
+
+  // merge the pair: each wave finalises half of the output tiles, taking the
+  // other half's partial (and its max and sum) through LDS
+  constexpr int XH = XT / 2;
+  constexpr int kXchg = XH * 16 * kWave + 2 * kWave;  // floats per wave
+  const float l_tot = half_sum(l_run);
+  float* xw = reinterpret_cast<float*>(smem) + w * kXchg;
+  if (wave_live) {
+#pragma unroll
+    for (int x2 = 0; x2 < XH; ++x2) {
+      // the tiles the partner finalises (constant register indices, a select)
+      const f32x16 t = half ? o[x2] : o[XH + x2];
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<f32x4*>(xw + ((x2 * 4 + c) * kWave + lane) * 4) =
+            f32x4{t[4 * c], t[4 * c + 1], t[4 * c + 2], t[4 * c + 3]};
+    }
+    *reinterpret_cast<f32x2*>(xw + XH * 16 * kWave + 2 * lane) = f32x2{m_run, l_tot};
+  }
+  lds_barrier();
+  if (!wave_live) return;
+  const float* xp = reinterpret_cast<const float*>(smem) + (w ^ 4) * kXchg;
+  const f32x2 ml = *reinterpret_cast<const f32x2*>(xp + XH * 16 * kWave + 2 * lane);
+  const float M = fmaxf(m_run, ml[0]);
+  const float mu = M == kNegInf ? 0.f : M;
+  const float a_self = fast_exp2(m_run - mu), a_part = fast_exp2(ml[0] - mu);
+  const float Lt = l_tot * a_self + ml[1] * a_part;
+  if (half == 0 && a.lse != nullptr && kg == 0 && rvalid)
+    a.lse[(size_t)(r0 + pos) * Hq + head] = Lt > 0.f ? (M + fast_log2(Lt)) * kLn2 : kNegInf;
+  if (!rvalid) return;
+  const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
+  const float cs = a_self * inv, cp = a_part * inv;
+  uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)(r0 + pos) * Hq + head) * D + 4 * kg;
+#pragma unroll
+  for (int x2 = 0; x2 < XH; ++x2) {
+    const f32x16 t = half ? o[XH + x2] : o[x2];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const f32x4 pv = *reinterpret_cast<const f32x4*>(xp + ((x2 * 4 + h) * kWave + lane) * 4);
+      *reinterpret_cast<u32x2*>(dst + 32 * (half * XH + x2) + 8 * h) =
+          u32x2{pack_bf16x2_hw(t[4 * h] * cs + pv[0] * cp, t[4 * h + 1] * cs + pv[1] * cp),
+                pack_bf16x2_hw(t[4 * h + 2] * cs + pv[2] * cp, t[4 * h + 3] * cs + pv[3] * cp)};
+    }
+  }
+}
+
+template <int D, int NB, bool SC, bool FLAT>
+__global__ __launch_bounds__(2 * kThreads, 1) void prefill_pp_kernel(PrefillArgs a) {
+  __shared__ u32x4 smem[kPrefillPPLdsBytes<D, NB> / 16];
+  prefill_pp_body<D, NB, SC, FLAT>(a, blockIdx.x, smem);
+}
+
 // each pool addressable by one buffer descriptor (32-bit offsets)
 template <int D>
 bool prefill_flat(const PrefillArgs& a) {
@@ -672,16 +1072,17 @@ bool prefill_flat(const PrefillArgs& a) {
 template <int D>
 void launch_mma32(PrefillArgs a, hipStream_t stream) {
   const bool flat = prefill_flat<D>(a);
+  constexpr int T = 2 * kThreads;
   if (a.softcap > 0.f) {
     if (flat)
-      prefill_mma32_kernel<D, PKV_PREFILL_RING, true, true><<<a.num_items, kThreads, 0, stream>>>(a);
+      prefill_pp_kernel<D, PKV_PREFILL_RING, true, true><<<a.num_items, T, 0, stream>>>(a);
     else
-      prefill_mma32_kernel<D, PKV_PREFILL_RING, true, false><<<a.num_items, kThreads, 0, stream>>>(a);
+      prefill_pp_kernel<D, PKV_PREFILL_RING, true, false><<<a.num_items, T, 0, stream>>>(a);
   } else {
     if (flat)
-      prefill_mma32_kernel<D, PKV_PREFILL_RING, false, true><<<a.num_items, kThreads, 0, stream>>>(a);
+      prefill_pp_kernel<D, PKV_PREFILL_RING, false, true><<<a.num_items, T, 0, stream>>>(a);
     else
-      prefill_mma32_kernel<D, PKV_PREFILL_RING, false, false><<<a.num_items, kThreads, 0, stream>>>(a);
+      prefill_pp_kernel<D, PKV_PREFILL_RING, false, false><<<a.num_items, T, 0, stream>>>(a);
   }
 }
 
