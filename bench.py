@@ -69,7 +69,8 @@ def parse_args():
                    help="with --decode-only: run the split-K decode with this partition size "
                         "(0: the balanced split) instead of the workload's own")
     p.add_argument("--timeline", metavar="WORKLOAD", default=None,
-                   choices=["gemma_decode", "sliding_window_decode"],
+                   choices=["gemma_decode", "sliding_window_decode",
+                            "chunked_prefill_shared_prefix"],
                    help="per-workgroup phase breakdown of one decode launch of WORKLOAD; needs "
                         "the timeline build (PKV_LIBRARY=block_paged_kv_append_amd/libpkv_timeline.so)")
     return p.parse_args()
@@ -581,6 +582,83 @@ def calibrate_copy(torch):
     print(json.dumps({"calibration": "copy", "bytes_read": n, "bytes_written": n, "launches": 10}))
 
 
+def prefill_timeline(name, torch, pkv, wl, replays=40, raw_out=None):
+    """Per-workgroup entry and exit stamps of one prefill launch of the named
+    workload, taken by the timeline build of the library: the shader-clock
+    counter (s_memtime) and the constant-rate counter (s_memrealtime) at entry
+    and after the pair merge, so the line gives each workgroup's duration, the
+    clock it ran at, and its matrix-core cycles at the nominal 32 cycles per
+    32x32x16 product against its cycles."""
+    import ctypes
+
+    import numpy as np
+
+    lib = pkv.load_library()
+    if not hasattr(lib, "pkv_timeline_set"):
+        raise SystemExit("--timeline needs the timeline build: "
+                         "PKV_LIBRARY=block_paged_kv_append_amd/libpkv_timeline.so")
+    lib.pkv_timeline_set.argtypes = [ctypes.c_void_p]
+    lib.pkv_timeline_set.restype = None
+    lib.pkv_timeline_clock_khz.restype = ctypes.c_int
+    khz = lib.pkv_timeline_clock_khz()
+    case = getattr(wl, name)()
+    dt = case.dtype
+    kp, vp = pkv.from_bits(case.k_pool, dt), pkv.from_bits(case.v_pool, dt)
+    q = pkv.from_bits(case.q, dt)
+    out = torch.empty_like(q)
+    cu = torch.from_numpy(case.cu_q_lens).cuda()
+    bt = torch.from_numpy(case.block_tables).cuda()
+    cl = torch.from_numpy(case.context_lens).cuda()
+    buf = torch.zeros(TL_WGS * TL_STAMPS, dtype=torch.int64, device="cuda")
+    lib.pkv_timeline_set(buf.data_ptr())
+
+    def calls():
+        for _ in range(PREFILL_REPEAT):
+            pkv.paged_attn_prefill(out, q, cu, case.max_q_len, kp, vp, bt, cl,
+                                   case.max_context_len, case.scale, case.softcap, case.window)
+
+    calls()
+    torch.cuda.synchronize()
+    g = capture(torch, calls)
+    warm(g, torch)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    buf.zero_()
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    per_call_us = e0.elapsed_time(e1) * 1e3 / (replays * PREFILL_REPEAT)
+    lib.pkv_timeline_set(None)
+    st = buf.view(TL_WGS, TL_STAMPS).cpu().numpy().astype(np.int64)
+    live = st[:, 3] != 0
+    s = st[live]
+    if raw_out:
+        np.save(raw_out, s[:, :8])
+    cycles = (s[:, 1] - s[:, 0]).astype(np.float64)
+    wg_us = (s[:, 3] - s[:, 2]) * 1e3 / khz
+    mhz = cycles / wg_us
+    stages = s[:, 4].astype(np.float64)
+    products = stages * (case.head_dim // 8)  # per SIMD: D/16 + D/16 per stage
+    span_us = float((s[:, 3].max() - s[:, 2].min()) * 1e3 / khz)
+
+    def pct(x):
+        x = np.asarray(x, dtype=np.float64)
+        return {k: round(float(np.percentile(x, q_)), 3)
+                for k, q_ in (("min", 0), ("p10", 10), ("p50", 50), ("p90", 90), ("max", 100))}
+
+    tiles = s[:, 5]
+    by_tile = {int(t): round(float(wg_us[tiles == t].mean()), 2) for t in np.unique(tiles)}
+    return {
+        "timeline": name, "workgroups": int(live.sum()), "clock_khz": khz,
+        "per_call_us_events": round(per_call_us, 2), "span_us": round(span_us, 2),
+        "shader_clock_mhz": pct(mhz), "workgroup_us": pct(wg_us),
+        "workgroup_cycles": pct(cycles), "stages": pct(stages),
+        "matrix_core_frac_nominal": pct(products * 32 / cycles),
+        "workgroup_us_by_tile": by_tile,
+    }
+
+
 # ---------------------------------------------------------------------------
 # timeline: where one decode launch spends its time (timeline build only)
 # ---------------------------------------------------------------------------
@@ -764,8 +842,8 @@ def main():
 
     pkv.load_library()  # raises if libpkv.so is missing: there is no fallback
     if args.timeline:
-        print(json.dumps(timeline(args.timeline, torch, pkv, wl, raw_out=args.timeline_raw)),
-              flush=True)
+        fn = prefill_timeline if args.timeline == "chunked_prefill_shared_prefix" else timeline
+        print(json.dumps(fn(args.timeline, torch, pkv, wl, raw_out=args.timeline_raw)), flush=True)
         return
     if args.copy_only:
         c = wl.gemma_decode()

@@ -18,7 +18,8 @@ namespace {
 thread_local char g_err[512] = "";
 
 #ifdef PKV_TIMELINE
-// timeline build: where the decode kernels write their phase stamps
+// timeline build: where the decode kernels write their phase stamps (and the
+// prefill its entry and exit stamps)
 unsigned long long* g_timeline = nullptr;
 #endif
 
@@ -608,6 +609,9 @@ int prefill_build(const char* fn, void* out, float* lse, const void* q, const in
   const long long items = (long long)num_seqs * num_kv_heads * a.tiles_per_seq;
   if (items > INT_MAX) return fail(PKV_EINVAL, "%s: %lld work items exceed the grid limit", fn, items);
   a.num_items = (int32_t)items;
+#ifdef PKV_TIMELINE
+  a.timeline = g_timeline;
+#endif
   *empty = false;
   return PKV_OK;
 }

@@ -100,6 +100,9 @@ struct PrefillArgs {
   float softcap;
   int32_t tiles_per_seq;  // work items per (sequence, kv head)
   int32_t num_items;      // grid size
+  // timeline build (PKV_TIMELINE) only: per-workgroup entry and exit stamps
+  // [kTimelineWgs][kTimelineStamps]; null otherwise, and never written
+  unsigned long long* timeline;
 };
 
 // Decode workspace geometry: the per-segment piece counters (fixed size, at

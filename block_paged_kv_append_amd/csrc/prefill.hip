@@ -715,6 +715,14 @@ __device__ __forceinline__ void prefill_pp_body(const PrefillArgs& a, int blk, u
   const bool flip_q = !SC && xf.scale_log2 < 0.f;
   const float pos_scale_log2 = fmaxf(fabsf(xf.scale_log2), 1e-30f);
 
+#ifdef PKV_TIMELINE
+  // timeline build: shader-clock and real-time counters at entry and exit
+  unsigned long long tl_cyc0 = 0, tl_rt0 = 0;
+  if (threadIdx.x == 0) {
+    tl_cyc0 = __builtin_amdgcn_s_memtime();
+    tl_rt0 = __builtin_amdgcn_s_memrealtime();
+  }
+#endif
   int item = blk;
   if (a.num_items % 8 == 0) item = (int)((unsigned)blk % 8u) * (a.num_items / 8) + (int)((unsigned)blk / 8u);
   const int tile = item % a.tiles_per_seq;
@@ -1031,6 +1039,17 @@ __device__ __forceinline__ void prefill_pp_body(const PrefillArgs& a, int blk, u
     *reinterpret_cast<f32x2*>(xw + XH * 16 * kWave + 2 * lane) = f32x2{m_run, l_tot};
   }
   lds_barrier();
+#ifdef PKV_TIMELINE
+  if (threadIdx.x == 0 && a.timeline != nullptr && blk < kTimelineWgs) {
+    unsigned long long* tl = a.timeline + (size_t)blk * kTimelineStamps;
+    tl[0] = tl_cyc0;
+    tl[1] = __builtin_amdgcn_s_memtime();
+    tl[2] = tl_rt0;
+    tl[3] = __builtin_amdgcn_s_memrealtime();
+    tl[4] = (unsigned long long)nstage;
+    tl[5] = (unsigned long long)tile;
+  }
+#endif
   if (!wave_live) return;
   const float* xp = reinterpret_cast<const float*>(smem) + (w ^ 4) * kXchg;
   const f32x2 ml = *reinterpret_cast<const f32x2*>(xp + XH * 16 * kWave + 2 * lane);
