@@ -569,6 +569,32 @@ def gemm_rate(torch) -> float:
     return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
 
 
+def mfma_rate(torch, pkv):
+    """The matrix-core rate this GPU sustains with every SIMD issuing
+    back-to-back bf16 32x32x16 products (the library's probe, one workgroup of
+    four waves per compute unit, about 2 ms), and the shader clock the SIMDs
+    ran at: (TFLOP/s, MHz, cycles per product), all medians over workgroups
+    except the rate (all products over the launch's HIP-event time)."""
+    import numpy as np
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 2000
+    stamps = torch.zeros(4 * cus, dtype=torch.int64, device="cuda")
+    pkv.mfma_rate_probe(stamps, iters, num_wgs=cus)  # warm-up
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    pkv.mfma_rate_probe(stamps, iters, num_wgs=cus)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    s = stamps.cpu().numpy().reshape(cus, 4).astype(np.float64)
+    cycles, ticks = s[:, 1] - s[:, 0], s[:, 3] - s[:, 2]
+    flops = cus * 4 * iters * 8 * 32768.0
+    return (flops / (ms * 1e-3) / 1e12, float(np.median(cycles / ticks * 100.0)),
+            float(np.median(cycles / (iters * 8))))
+
+
 def calibrate_copy(torch):
     """A plain device-to-device copy of 1 GiB, 10 times: the reference for
     scaling the HBM FETCH_SIZE / WRITE_SIZE counters."""
@@ -984,6 +1010,11 @@ def main():
         gr = gemm_rate(torch)
         line["box_gemm_tflops"] = round(gr, 1)
         line["prefill"]["roofline"]["frac_of_box_gemm"] = round(line["prefill"]["tflops"] / gr, 4)
+        mr, mhz, cpp = mfma_rate(torch, pkv)
+        line["box_mfma_tflops"] = round(mr, 1)
+        line["box_mfma_clock_mhz"] = round(mhz)
+        line["box_mfma_cycles_per_product"] = round(cpp, 2)
+        line["prefill"]["roofline"]["frac_of_box_mfma"] = round(line["prefill"]["tflops"] / mr, 4)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(line), flush=True)

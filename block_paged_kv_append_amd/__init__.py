@@ -67,6 +67,7 @@ SIGNATURES = {
     "pkv_check_paged_metadata": (ctypes.c_int, [_P, _P, _I, _I, _I, _P, _I, _P, _P]),
     "pkv_hbm_read_probe": (ctypes.c_int, [_P, _Z, _P, _I, _P]),
     "pkv_hbm_gather_probe": (ctypes.c_int, [_P, _P, _Z, _I, _P, _I, _P, _I, _P]),
+    "pkv_mfma_rate_probe": (ctypes.c_int, [_P, _I, _I, _P]),
     "pkv_last_error": (ctypes.c_char_p, []),
 }
 
@@ -548,6 +549,22 @@ def hbm_gather_probe(k, v, order, out, num_wgs=None, stream=None) -> None:
     _check("pkv_hbm_gather_probe",
            lib.pkv_hbm_gather_probe(_ptr(k), _ptr(v), block_bytes, nb, _i32(order, "order"),
                                     order.numel(), _ptr(out), int(n), _stream(stream)))
+
+
+def mfma_rate_probe(stamps, iters, num_wgs=None, stream=None) -> None:
+    """Back-to-back bf16 32x32x16 matrix-core products, ``iters`` x 8 per wave,
+    in ``num_wgs`` workgroups of four waves (default: one per compute unit);
+    ``stamps`` (int64 device tensor, at least 4 num_wgs entries) receives per
+    workgroup the shader-clock counter before and after the loop, then the
+    100 MHz counter before and after."""
+    import torch
+
+    n = num_wgs or torch.cuda.get_device_properties(stamps.device).multi_processor_count
+    if stamps.numel() < 4 * n or stamps.element_size() != 8:
+        raise ValueError("stamps needs 4 num_wgs 64-bit entries")
+    lib = load_library()
+    _check("pkv_mfma_rate_probe",
+           lib.pkv_mfma_rate_probe(_ptr(stamps), int(iters), int(n), _stream(stream)))
 
 
 def from_bits(bits, dtype: str, device="cuda"):

@@ -384,6 +384,16 @@ int pkv_hbm_read_probe(const void* buf, size_t bytes, uint32_t* out, int32_t num
                                        reinterpret_cast<hipStream_t>(stream)), fn);
 }
 
+int pkv_mfma_rate_probe(unsigned long long* stamps, int32_t iters, int32_t num_wgs,
+                        struct ihipStream_t* stream) {
+  const char* fn = "pkv_mfma_rate_probe";
+  if (stamps == nullptr || !aligned(stamps, 8)) return fail(PKV_EINVAL, "%s: stamps null or misaligned", fn);
+  if (iters < 1 || iters > (1 << 24)) return fail(PKV_EINVAL, "%s: iters %d", fn, iters);
+  if (num_wgs < 1 || num_wgs > (1 << 20)) return fail(PKV_EINVAL, "%s: num_wgs %d", fn, num_wgs);
+  return from_hip(pkv::launch_mfma_rate(stamps, iters, num_wgs, reinterpret_cast<hipStream_t>(stream)),
+                  fn);
+}
+
 int pkv_hbm_gather_probe(const void* k, const void* v, size_t block_bytes, int32_t num_blocks,
                          const int32_t* order, int32_t n, uint32_t* out, int32_t num_wgs,
                          struct ihipStream_t* stream) {

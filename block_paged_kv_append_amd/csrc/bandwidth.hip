@@ -79,6 +79,47 @@ __global__ __launch_bounds__(kReadThreads) void hbm_gather_kernel(const u32x4* k
   }
 }
 
+// Back-to-back 32x32x16 bf16 matrix-core products, one wave per SIMD (a
+// workgroup of four waves per CU): the product rate and the shader clock this
+// GPU sustains with every matrix core busy, beside the prefill (whose
+// throughput is judged against the matrix-core peak).  Four independent
+// accumulators, so no product waits for the previous one; lane 0 of each
+// workgroup records the shader-clock counter and the constant-rate counter
+// before and after the loop.  No memory access inside the loop.
+__global__ __launch_bounds__(kReadThreads) void mfma_rate_kernel(unsigned long long* stamps, int iters) {
+  bf16x8 a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(0.001f * (float)(threadIdx.x + i));
+    b[i] = (__bf16)(0.002f * (float)i);
+  }
+  f32x16 c0 = {}, c1 = {}, c2 = {}, c3 = {};
+  const unsigned long long t0 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c1, 0, 0, 0);
+      c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c2, 0, 0, 0);
+      c3 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c3, 0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const unsigned long long t1 = __builtin_amdgcn_s_memtime();
+  const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
+  // keeps the products live: the operands are non-negative, so the sum is
+  // never -1 and the record always holds the end stamp
+  const float sink = c0[0] + c1[1] + c2[2] + c3[3];
+  if (threadIdx.x == 0) {
+    unsigned long long* s = stamps + (size_t)blockIdx.x * 4;
+    s[0] = t0;
+    s[1] = t1;
+    s[2] = r0;
+    s[3] = sink == -1.0f ? 0ull : r1;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_hbm_gather(const void* k, const void* v, size_t block_bytes, int num_blocks,
@@ -88,6 +129,12 @@ hipError_t launch_hbm_gather(const void* k, const void* v, size_t block_bytes, i
   hbm_gather_kernel<<<num_wgs, kReadThreads, 0, stream>>>(
       reinterpret_cast<const u32x4*>(k), reinterpret_cast<const u32x4*>(v), order, n, num_blocks,
       (int)(block_bytes / 16), out);
+  return hipGetLastError();
+}
+
+hipError_t launch_mfma_rate(unsigned long long* stamps, int iters, int num_wgs, hipStream_t stream) {
+  if (iters <= 0 || num_wgs <= 0) return hipSuccess;
+  mfma_rate_kernel<<<num_wgs, kReadThreads, 0, stream>>>(stamps, iters);
   return hipGetLastError();
 }
 

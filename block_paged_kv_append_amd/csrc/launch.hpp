@@ -138,6 +138,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 // out [num_wgs] receives one folded word each
 hipError_t launch_hbm_read(const void* buf, size_t bytes, uint32_t* out, int num_wgs,
                            hipStream_t stream);
+// back-to-back 32x32x16 bf16 products, four waves per workgroup; stamps[4 w .. 4 w + 3]
+hipError_t launch_mfma_rate(unsigned long long* stamps, int iters, int num_wgs, hipStream_t stream);
 // a gather of whole blocks order[0..n) of two pools of num_blocks blocks
 // (block_bytes each, a multiple of 4096; entries outside read block 0)
 hipError_t launch_hbm_gather(const void* k, const void* v, size_t block_bytes, int num_blocks,

@@ -483,6 +483,21 @@ int pkv_hbm_gather_probe(const void* k, const void* v, size_t block_bytes, int32
                          const int32_t* order, int32_t n, uint32_t* out, int32_t num_wgs,
                          struct ihipStream_t* stream);
 
+/*
+ * pkv_mfma_rate_probe -- a measurement aid beside the prefill: num_wgs
+ * workgroups of four waves (one per SIMD when num_wgs equals the CU count)
+ * each run iters x 8 back-to-back bf16 32x32x16 matrix-core products (32768
+ * flops per product per wave) with no memory access, and lane 0 writes four
+ * counters to stamps[4 w .. 4 w + 3] (caller-owned device memory, 8-byte
+ * aligned): the shader-clock counter before and after the loop, then the
+ * constant-rate (100 MHz) counter before and after.  From them: cycles per
+ * product, the clock the SIMDs ran at, and the sustained product rate.
+ * PKV_EINVAL for a null or misaligned buffer, iters outside [1, 2^24] or
+ * num_wgs outside [1, 2^20].
+ */
+int pkv_mfma_rate_probe(unsigned long long* stamps, int32_t iters, int32_t num_wgs,
+                        struct ihipStream_t* stream);
+
 /* Message describing the calling thread's last failed call ("" if none). */
 const char* pkv_last_error(void);
 

@@ -152,3 +152,23 @@ def test_hbm_gather_probe_reads_each_listed_block_once():
         want = np.bitwise_xor.reduce(np.bitwise_xor.reduce(k[ids], axis=1) ^
                                      np.bitwise_xor.reduce(v[ids], axis=1))
         assert got == want
+
+
+def test_mfma_rate_probe_records_every_workgroup():
+    """The matrix-core rate probe writes, per workgroup, shader-clock and
+    100 MHz counter pairs that advance over the loop; the cycles per product
+    are at least the 32 a 32x32x16 bf16 product takes (8 passes of 4 cycles)
+    and the implied clock lies in the part's range."""
+    wgs, iters = 8, 2000
+    print("\n[case] matrix-core rate probe", wgs, iters, flush=True)
+    stamps = torch.zeros(4 * wgs, dtype=torch.int64, device="cuda")
+    pkv.mfma_rate_probe(stamps, iters, num_wgs=wgs)
+    torch.cuda.synchronize()
+    s = stamps.cpu().numpy().reshape(wgs, 4).astype(np.float64)
+    cycles, ticks = s[:, 1] - s[:, 0], s[:, 3] - s[:, 2]
+    assert np.all(cycles > 0) and np.all(ticks > 0)
+    per_product = cycles / (iters * 8)
+    assert np.all(per_product >= 32) and np.all(per_product < 200), per_product
+    mhz = cycles / ticks * 100.0
+    assert np.all((mhz > 500) & (mhz < 3000)), mhz
+
