@@ -15,6 +15,8 @@
 // row.  Only blocks on the causal diagonal (or at a window edge) are partly
 // masked; masking is by select.  Workgroups are numbered so that all ranges
 // of one (sequence, kv head) land on the same XCD and share its L2.
+#include <type_traits>
+
 #include "attn_tile.hpp"
 #include "launch.hpp"
 
@@ -908,10 +910,11 @@ __device__ __forceinline__ void prefill_pp_body(const PrefillArgs& a, int blk, u
     }
     const int slot = st & (NB - 1);
 
-    // S^T = K Q^T, with this interval's copies issued in its shadow
+    // S^T = K Q^T, with this interval's copies issued in its shadow (two
+    // instances of the loop, so that no branch sits between the products)
     const u32x4* kb = smem + slot * kStageU4 + k_rd;
     f32x16 acc = {};
-    {
+    auto qk = [&](auto with_copies) {
       u32x4 kf[kAhead];
 #pragma unroll
       for (int i = 0; i < kAhead; ++i) kf[i] = kb[k_run(i)];
@@ -920,10 +923,16 @@ __device__ __forceinline__ void prefill_pp_body(const PrefillArgs& a, int blk, u
         __builtin_amdgcn_sched_barrier(0);
         acc = mma32_bf16(kf[i % kAhead], qf[i], acc);
         if (i + kAhead < KD) kf[i % kAhead] = kb[k_run(i + kAhead)];
-        if ((i & 1) == 0 && do_copy) copy(i >> 1);
+        if constexpr (decltype(with_copies)::value) {
+          if ((i & 1) == 0) copy(i >> 1);
+        }
       }
-    }
-    __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (do_copy)
+      qk(std::true_type{});
+    else
+      qk(std::false_type{});
 
     // keys past the context (or of an unreadable block): their V entries are
     // cleared in LDS before the products read them (every wave computing this
