@@ -289,6 +289,39 @@ def test_prefill_small(spec):
     check_lse(lse, ref_lse, "prefill")
 
 
+# Stage counts at the edges of the two-wave prefill's interval structure
+# (waves w and w + 4 take alternate 32-key stages; copies run one interval
+# ahead through a four-stage ring): a single stage (the odd half computes
+# nothing), two, three, tails of 1, 15, 16 and 17 keys, and a window whose
+# first visible block is not block 0.  Chunks equal to the context make every
+# stage a diagonal one.
+STAGE_EDGES = [
+    # (cached, chunk, Hq, Hkv, D, softcap, window)
+    ([0, 0, 0, 0], [5, 16, 31, 32], 8, 2, 256, 0.0, 0),
+    ([0, 1, 0, 16], [33, 47, 64, 49], 8, 2, 256, 0.0, 0),
+    ([65, 96, 0], [1, 31, 97], 4, 1, 64, 20.0, 0),
+    ([200, 31], [40, 70], 8, 2, 128, 0.0, 37),
+    ([17, 0], [111, 129], 16, 2, 256, 0.0, 48),
+]
+
+
+@pytest.mark.parametrize("spec", STAGE_EDGES,
+                         ids=lambda s: f"D{s[4]}-G{s[2]//s[3]}-{'-'.join(map(str, s[1]))}-w{s[6]}")
+def test_prefill_stage_count_edges(spec):
+    cached, chunk, Hq, Hkv, D, cap, W = spec
+    case = wl.make_prefill_case(900 + D + sum(chunk), cached, chunk, Hq, Hkv, D, "bf16",
+                                softcap=cap, window=W)
+    banner("prefill stage edges", spec)
+    kp, vp = run_append(case)
+    out, lse = run_prefill(case, kp, vp)
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool,
+                           "bf16")
+    ref, ref_lse = oracle.prefill(case.q, case.cu_q_lens, kr, vr, case.block_tables,
+                                  case.context_lens, case.scale, case.softcap, case.window, "bf16")
+    check_close(out, ref, "bf16", "prefill stage edges")
+    check_lse(lse, ref_lse, "prefill stage edges")
+
+
 @pytest.mark.parametrize("q_scale", [1.0, 8.0], ids=["plain", "peaked"])
 def test_chunked_prefill_full(q_scale):
     case = wl.chunked_prefill_shared_prefix(q_scale=q_scale)
