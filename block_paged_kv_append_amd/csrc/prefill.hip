@@ -1039,7 +1039,9 @@ __device__ __forceinline__ void prefill_pp_body(const PrefillArgs& a, int blk, u
 #pragma unroll
     for (int x2 = 0; x2 < XH; ++x2) {
       // the tiles the partner finalises (constant register indices, a select)
-      const f32x16 t = half ? o[x2] : o[XH + x2];
+      f32x16 t;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) t[e] = half ? o[x2][e] : o[XH + x2][e];
 #pragma unroll
       for (int c = 0; c < 4; ++c)
         *reinterpret_cast<f32x4*>(xw + ((x2 * 4 + c) * kWave + lane) * 4) =
@@ -1060,27 +1062,54 @@ __device__ __forceinline__ void prefill_pp_body(const PrefillArgs& a, int blk, u
   }
 #endif
   if (!wave_live) return;
-  const float* xp = reinterpret_cast<const float*>(smem) + (w ^ 4) * kXchg;
+  // the partner's exchange area: its partial of this wave's half, read whole
+  // into registers first (after that nobody reads this area again, and it
+  // stages this wave's output rows below)
+  float* xp = reinterpret_cast<float*>(smem) + (w ^ 4) * kXchg;
   const f32x2 ml = *reinterpret_cast<const f32x2*>(xp + XH * 16 * kWave + 2 * lane);
+  f32x4 pv[XH * 4];
+#pragma unroll
+  for (int q = 0; q < XH * 4; ++q) pv[q] = *reinterpret_cast<const f32x4*>(xp + (q * kWave + lane) * 4);
   const float M = fmaxf(m_run, ml[0]);
   const float mu = M == kNegInf ? 0.f : M;
   const float a_self = fast_exp2(m_run - mu), a_part = fast_exp2(ml[0] - mu);
   const float Lt = l_tot * a_self + ml[1] * a_part;
   if (half == 0 && a.lse != nullptr && kg == 0 && rvalid)
     a.lse[(size_t)(r0 + pos) * Hq + head] = Lt > 0.f ? (M + fast_log2(Lt)) * kLn2 : kNegInf;
-  if (!rvalid) return;
   const float inv = Lt > 0.f ? 1.0f / Lt : 0.f;
   const float cs = a_self * inv, cp = a_part * inv;
-  uint16_t* dst = reinterpret_cast<uint16_t*>(a.out) + ((size_t)(r0 + pos) * Hq + head) * D + 4 * kg;
+  // The rows leave through LDS so that a wave writes whole 128-byte lines (a
+  // row's half is D bytes: D / 16 lanes of 16 bytes) with streaming stores,
+  // which go to memory as the workgroup finishes instead of waiting in L2 as
+  // partial lines.  Staged row-halves are padded by 16 bytes against bank
+  // conflicts.
+  constexpr int kRowU32 = D / 4 + 4;
+  uint32_t* stage = reinterpret_cast<uint32_t*>(xp);
 #pragma unroll
   for (int x2 = 0; x2 < XH; ++x2) {
-    const f32x16 t = half ? o[XH + x2] : o[x2];
+    f32x16 t;  // this wave's tile (element-wise select: the array stays in registers)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) t[e] = half ? o[XH + x2][e] : o[x2][e];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const f32x4 pv = *reinterpret_cast<const f32x4*>(xp + ((x2 * 4 + h) * kWave + lane) * 4);
-      *reinterpret_cast<u32x2*>(dst + 32 * (half * XH + x2) + 8 * h) =
-          u32x2{pack_bf16x2_hw(t[4 * h] * cs + pv[0] * cp, t[4 * h + 1] * cs + pv[1] * cp),
-                pack_bf16x2_hw(t[4 * h + 2] * cs + pv[2] * cp, t[4 * h + 3] * cs + pv[3] * cp)};
+      const f32x4 v = pv[x2 * 4 + h];
+      *reinterpret_cast<u32x2*>(stage + n * kRowU32 + 16 * x2 + 4 * h + 2 * kg) =
+          u32x2{pack_bf16x2_hw(t[4 * h] * cs + v[0] * cp, t[4 * h + 1] * cs + v[1] * cp),
+                pack_bf16x2_hw(t[4 * h + 2] * cs + v[2] * cp, t[4 * h + 3] * cs + v[3] * cp)};
+    }
+  }
+  wait_lds();
+  constexpr int kLanesPerRow = D / 16;  // 16-byte pieces of a row-half
+  constexpr int kRowsPerStep = kWave / kLanesPerRow;
+  const int col = lane % kLanesPerRow;
+#pragma unroll
+  for (int r0w = 0; r0w < 32; r0w += kRowsPerStep) {
+    const int r = r0w + lane / kLanesPerRow;
+    const int rpos = pos_wave + r / G;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(stage + r * kRowU32 + 4 * col);
+    if (rpos < nq) {
+      uint16_t* row = reinterpret_cast<uint16_t*>(a.out) + ((size_t)(r0 + rpos) * Hq + g * G + r % G) * D;
+      __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(row + half * (D / 2) + 8 * col));
     }
   }
 }
