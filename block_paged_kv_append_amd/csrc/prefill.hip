@@ -6,15 +6,21 @@
 // Map", section "How a single request flows through the system" -- a long
 // prompt is prefilled one chunk per tick, after the cached prefix.
 //
-// Query rows are packed by GQA group: a 16-row matrix-core tile holds
-// 16 / G consecutive positions times the G query heads that share one kv
-// head, so each K/V block loaded serves G heads at once.  A workgroup is one
-// (sequence, kv head, range of positions); each of its four waves owns RT
-// row tiles and walks every cache block its rows can see, double-buffered,
+// Query rows are packed by GQA group: a matrix-core tile holds consecutive
+// positions times the G query heads that share one kv head, so each K/V
+// block loaded serves G heads at once.  A workgroup is one (sequence, kv
+// head, range of positions) and walks every cache block its rows can see,
 // running S^T = K Q^T and P V on the matrix cores with an online softmax per
 // row.  Only blocks on the causal diagonal (or at a window edge) are partly
 // masked; masking is by select.  Workgroups are numbered so that all ranges
-// of one (sequence, kv head) land on the same XCD and share its L2.
+// of one (sequence, kv head) land on the same XCD and share its L2.  Three
+// forms:
+//   * fp32 pools (prefill_kernel): 16-row tiles, blocks through registers;
+//   * bf16 (prefill_pp_kernel): 32-row tiles on 32x32x16 products, stages of
+//     32 keys streamed to LDS, two waves per SIMD sharing their rows and
+//     splitting the stages (the prefill entry point);
+//   * bf16, one wave per SIMD (prefill_mma32_body): the prefill part of the
+//     one-launch mixed batch, whose decode workgroups run four waves.
 #include <type_traits>
 
 #include "attn_tile.hpp"
@@ -277,9 +283,8 @@ template <int D, int NB>
 constexpr size_t kPrefillLdsBytes = (size_t)NB * kPrefillStageU4<D, NB> * 16;
 
 // The prefill of work item `blk` (before the XCD-aware renumbering), with
-// `smem` its stage ring in LDS.  prefill_mma32_kernel runs it for its own
-// workgroup; the mixed-batch kernel runs it for the first workgroups of its
-// grid.
+// `smem` its stage ring in LDS, by four waves: the mixed-batch kernel runs it
+// for the first workgroups of its grid.
 template <int D, int NB, bool SC, bool FLAT>
 __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk, u32x4* smem) {
   constexpr int KD = D / 16;                    // K runs per stage = QK products
@@ -659,12 +664,6 @@ __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk
       *reinterpret_cast<u32x2*>(dst + 32 * x + 8 * h) =
           u32x2{pack_bf16x2_hw(o[x][4 * h] * inv, o[x][4 * h + 1] * inv),
                 pack_bf16x2_hw(o[x][4 * h + 2] * inv, o[x][4 * h + 3] * inv)};
-}
-
-template <int D, int NB, bool SC, bool FLAT>
-__global__ __launch_bounds__(kThreads, 1) void prefill_mma32_kernel(PrefillArgs a) {
-  __shared__ u32x4 smem[NB * kPrefillStageU4<D, NB>];
-  prefill_mma32_body<D, NB, SC, FLAT>(a, blockIdx.x, smem);
 }
 
 // ---------------------------------------------------------------------------
