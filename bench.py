@@ -68,6 +68,9 @@ def parse_args():
     p.add_argument("--partition-size", type=int, default=None,
                    help="with --decode-only: run the split-K decode with this partition size "
                         "(0: the balanced split) instead of the workload's own")
+    p.add_argument("--mixed-only", action="store_true",
+                   help="time only the mixed batch (one launch, one prefill launch, prefill then "
+                        "decode) and print one JSON line")
     p.add_argument("--timeline", metavar="WORKLOAD", default=None,
                    choices=["gemma_decode", "sliding_window_decode",
                             "chunked_prefill_shared_prefix"],
@@ -387,7 +390,8 @@ def time_mixed(torch, pkv, wl, iters=20):
     decode rows (contexts uniform in [512, 4096]), 8 q / 2 kv heads, D 256,
     bf16.  Times paged_attn_mixed (one launch: the chunks through the prefill
     body, the decode rows through the balanced decode split beside them) and,
-    for comparison, the same batch through one prefill launch."""
+    for comparison, the same batch through one prefill launch, and through a
+    prefill launch for the chunks followed by a decode launch for the rows."""
     import numpy as np
 
     rng = np.random.default_rng(6)
@@ -417,8 +421,18 @@ def time_mixed(torch, pkv, wl, iters=20):
             pkv.paged_attn_prefill(out, q, cu_all, 512, kp, vp, bt, cl, c.max_context_len,
                                    c.scale, c.softcap, 0)
 
+    P = 4 * 512  # the chunks' rows; the decode rows follow them
+    bt4, cl4 = bt[4:].contiguous(), cl[4:].contiguous()
+
+    def two_launches():  # the chunks through the prefill, then the rows through the decode
+        for _ in range(4):
+            pkv.paged_attn_prefill(out[:P], q[:P], cu4, 512, kp, vp, bt[:4], cl[:4],
+                                   c.max_context_len, c.scale, c.softcap, 0)
+            pkv.paged_attn_decode(out[P:], q[P:], kp, vp, bt4, cl4, c.max_context_len, c.scale,
+                                  c.softcap, 0, workspace=ws)
+
     res = []
-    for fn in (mixed, one_prefill):
+    for fn in (mixed, one_prefill, two_launches):
         fn()
         torch.cuda.synchronize()
         g = capture(torch, fn)
@@ -431,7 +445,7 @@ def time_mixed(torch, pkv, wl, iters=20):
             ev[i][1].record()
         torch.cuda.synchronize()
         res.append(float(np.mean([a.elapsed_time(b) for a, b in ev])) / 4)
-    return res[0], res[1]
+    return res[0], res[1], res[2]
 
 
 def time_eviction(torch, pkv, wl):
@@ -892,6 +906,11 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(torch)
         return
+    if args.mixed_only:
+        mx_ms, one_ms, two_ms = time_mixed(torch, pkv, wl)
+        print(json.dumps({"mixed_call_ms": round(mx_ms, 5), "one_prefill_launch_ms": round(one_ms, 5),
+                          "prefill_then_decode_ms": round(two_ms, 5)}))
+        return
     if args.prefill_only:
         pc = wl.chunked_prefill_shared_prefix()
         app_ms, pre_ms = time_prefill(pc, 20, 3, torch, pkv)
@@ -975,11 +994,12 @@ def main():
         line["copy_blocks"] = {"pairs": cb_pairs, "ms": round(cb_ms, 5),
                                "gbs": round(cb_bytes / (cb_ms * 1e-3) / 1e9, 1), "bytes": cb_bytes,
                                "pool": "gemma_decode (2 kv heads, D256, bf16: 32 KiB per pair)"}
-        mx_ms, one_ms = time_mixed(torch, pkv, wl)
+        mx_ms, one_ms, two_ms = time_mixed(torch, pkv, wl)
         line["mixed_batch"] = {
             "workload": "4 prefill chunks (2048 cached + 512) + 28 decode rows (ctx U[512,4096]), "
                         "8q/2kv heads, D256, bf16, softcap 50",
-            "mixed_call_ms": round(mx_ms, 5), "one_prefill_launch_ms": round(one_ms, 5)}
+            "mixed_call_ms": round(mx_ms, 5), "one_prefill_launch_ms": round(one_ms, 5),
+            "prefill_then_decode_ms": round(two_ms, 5)}
         for maker in (wl.sliding_window_decode, wl.long_context_splitk):
             c = maker()
             b = DecodeBench(c, 0, torch, pkv)
