@@ -841,7 +841,12 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
 // one workgroup per partition (same partials, same merge), without a round of
 // workgroup start-ups per partition.
 // ---------------------------------------------------------------------------
-constexpr int kStreamRingBytes = 32768;  // per wave
+// per wave: two blocks in flight at head_dim 256 and 128 (four at 64).  At
+// head_dim 128 a 32 KiB ring (four blocks) measured 1.3% slower on the long-
+// context split-K shape: with every CU streaming, fewer bytes in flight per CU
+// serve the memory system better.
+template <int D>
+constexpr int kStreamRingBytes = D >= 256 ? 32768 : 16384;
 constexpr int kDummyBytes = 1024;        // takes the empty prologue copies
 template <int D>
 __host__ __device__ constexpr int combine_bytes(int G) {
@@ -850,7 +855,7 @@ __host__ __device__ constexpr int combine_bytes(int G) {
 }
 template <int D>
 __host__ __device__ constexpr int fixed_stream_lds(int G) {
-  return kWaves * kStreamRingBytes + combine_bytes<D>(G) + kDummyBytes;
+  return kWaves * kStreamRingBytes<D> + combine_bytes<D>(G) + kDummyBytes;
 }
 constexpr int kLdsPerCu = 163840;
 
@@ -880,7 +885,7 @@ __device__ void run_piece_stream(const DecodeArgs& a, const LogitXform& xf, cons
   constexpr int XT = D / 16;                        // output tiles
   constexpr int kTileBytes = D * kBlock * 2;        // one block's K (or V)
   constexpr int kRuns = 2 * kTileBytes / 1024;      // 1 KiB copies per block
-  constexpr int NS = kStreamRingBytes / (2 * kTileBytes);
+  constexpr int NS = kStreamRingBytes<D> / (2 * kTileBytes);
   static_assert(NS >= 2 && (NS & (NS - 1)) == 0, "a power of two, at least two blocks in flight");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -948,7 +953,7 @@ __device__ void run_piece_stream(const DecodeArgs& a, const LogitXform& xf, cons
 
   const char* kpool = reinterpret_cast<const char*>(a.k_pool);
   const char* vpool = reinterpret_cast<const char*>(a.v_pool);
-  char* ring = reinterpret_cast<char*>(lds) + wave * kStreamRingBytes;
+  char* ring = reinterpret_cast<char*>(lds) + wave * kStreamRingBytes<D>;
   char* dummy = reinterpret_cast<char*>(cmb) + combine_bytes<D>(G);
   const int pos = __builtin_amdgcn_readfirstlane(rs.pos);
   uint32_t okbits = __builtin_amdgcn_readfirstlane(rs.okbits);
@@ -1088,7 +1093,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_fixed_stream_kernel(Decode
   const int NP = a.num_partitions, PB = a.part_blocks;
   const int N = gridDim.x, w = blockIdx.x;
   const int lane = threadIdx.x & 63;
-  float* cmb = lds + kWaves * kStreamRingBytes / 4;
+  float* cmb = lds + kWaves * kStreamRingBytes<D> / 4;
   auto span = [&](int L) { return seq_span(L, a.window, a.max_context_len); };
   // visible partitions of a sequence of length L
   auto parts = [&](int L) -> int {
