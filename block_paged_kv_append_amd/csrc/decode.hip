@@ -65,6 +65,11 @@ __device__ __forceinline__ float load_dev(const float* p) {
 // 16 bytes per load through a resource over the whole partials region (when
 // it spans less than 2 GiB; else per float).
 constexpr int kDeviceScope = 16;  // cache policy: sc1
+// Cache policy of the K/V copies into the rings: nontemporal.  A decode reads
+// every cache block once per launch, so streaming reads keep the blocks from
+// displacing anything in the caches (tick 36.0 -> 32.3 us, long-context
+// split-K 99.6 -> 88.2 us against the default policy).
+constexpr int kStreamLoad = 2;
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t region(void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(base, 0, bytes, 0x00020000u);
 }
@@ -769,11 +774,11 @@ __device__ void run_piece_ring(const DecodeArgs& a, const LogitXform& xf, const 
 #pragma unroll
     for (int r = 0; r < kRuns / 2; ++r)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dst + r * 1024),
-                                               16, r * 1024 + lane * 16, 0, 0, 0);
+                                               16, r * 1024 + lane * 16, 0, 0, kStreamLoad);
 #pragma unroll
     for (int r = 0; r < kRuns / 2; ++r)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(dst + kTileBytes + r * 1024),
-                                               16, r * 1024 + lane * 16, 0, 0, 0);
+                                               16, r * 1024 + lane * 16, 0, 0, kStreamLoad);
   };
 
 #pragma unroll
@@ -987,12 +992,12 @@ __device__ void run_piece_stream(const DecodeArgs& a, const LogitXform& xf, cons
 #pragma unroll
     for (int r = 0; r < kRuns / 2; ++r)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(dst + r * step),
-                                               16, r * 1024 + lane * 16, 0, 0, 0);
+                                               16, r * 1024 + lane * 16, 0, 0, kStreamLoad);
 #pragma unroll
     for (int r = 0; r < kRuns / 2; ++r)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rv, (__attribute__((address_space(3))) void*)(dst + (fake ? 0 : kTileBytes) + r * step), 16,
-          r * 1024 + lane * 16, 0, 0, 0);
+          r * 1024 + lane * 16, 0, 0, kStreamLoad);
   };
 
   // NS prologue copies on every path (fake ones when the partition before
