@@ -450,6 +450,11 @@ __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk
   // This wave's copy j of the prepared stage.  K runs 2p, 2p+1 form 2 KiB:
   // the first KiB from block 0 (run 2p's lanes n < 16, then run 2p+1's),
   // the second from block 1; each copy reads one block.
+  // With per-block descriptors (pools over 4 GiB) a copy's 1 KiB run offset
+  // goes to the scalar offset, so that all of a wave's copies share one
+  // lane-offset register for K and one for V: the descriptors take registers
+  // the loop would otherwise spill for.
+  const int k_lane = k_off * 16, v_lane = v_off * 16;
   auto copy = [&](int j) {
     if (j < KD / kWaves) {
       const int pr = 2 * j + (wave >> 1);
@@ -457,14 +462,14 @@ __device__ __forceinline__ void prefill_mma32_body(const PrefillArgs& a, int blk
       if constexpr (FLAT)
         copy_to_lds(rkp, (64 * pr + k_off) * 16, csoff, dst);
       else
-        copy_to_lds((wave & 1) ? crk1 : crk0, (64 * pr + k_off) * 16, 0, dst);
+        copy_to_lds((wave & 1) ? crk1 : crk0, k_lane, pr * 1024, dst);
     } else {
       const int x = 2 * (j - KD / kWaves) + (wave >> 1);
       u32x4* dst = cdst + (KD + 2 * x + (wave & 1)) * kWave;
       if constexpr (FLAT)
         copy_to_lds(rvp, (64 * x + v_off) * 16, csoff, dst);
       else
-        copy_to_lds((wave & 1) ? crv1 : crv0, (64 * x + v_off) * 16, 0, dst);
+        copy_to_lds((wave & 1) ? crv1 : crv0, v_lane, x * 1024, dst);
     }
   };
   auto issue = [&](int st) {
@@ -844,6 +849,11 @@ __device__ __forceinline__ void prefill_pp_body(const PrefillArgs& a, int blk, u
     tailbits = (tailbits & ~(1u << slot)) | ((uint32_t)tail << slot);
     cdst = smem + slot * kStageU4;
   };
+  // With per-block descriptors (pools over 4 GiB) a copy's 1 KiB run offset
+  // goes to the scalar offset, so that all of a wave's copies share one
+  // lane-offset register for K and one for V: the descriptors take registers
+  // the loop would otherwise spill for.
+  const int k_lane = k_off * 16, v_lane = v_off * 16;
   auto copy = [&](int j) {
     if (j < KD / kWaves) {
       const int pr = 2 * j + (wave >> 1);
@@ -851,14 +861,14 @@ __device__ __forceinline__ void prefill_pp_body(const PrefillArgs& a, int blk, u
       if constexpr (FLAT)
         copy_to_lds(rkp, (64 * pr + k_off) * 16, csoff, dst);
       else
-        copy_to_lds((wave & 1) ? crk1 : crk0, (64 * pr + k_off) * 16, 0, dst);
+        copy_to_lds((wave & 1) ? crk1 : crk0, k_lane, pr * 1024, dst);
     } else {
       const int x = 2 * (j - KD / kWaves) + (wave >> 1);
       u32x4* dst = cdst + (KD + 2 * x + (wave & 1)) * kWave;
       if constexpr (FLAT)
         copy_to_lds(rvp, (64 * x + v_off) * 16, csoff, dst);
       else
-        copy_to_lds((wave & 1) ? crv1 : crv0, (64 * x + v_off) * 16, 0, dst);
+        copy_to_lds((wave & 1) ? crv1 : crv0, v_lane, x * 1024, dst);
     }
   };
 
