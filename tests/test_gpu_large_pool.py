@@ -2,9 +2,9 @@
 blocks with per-block buffer descriptors (smaller pools use one descriptor
 per pool and 32-bit offsets), and every kernel forms byte offsets beyond
 2^32.  A small case is embedded in pools of 600000 blocks (4.9 GB each at
-2 kv heads x head_dim 128, bf16) at block ids near the end of the pool; the
-results must equal the oracle's on the small case (append bit-exact,
-attention to the bf16 tolerance)."""
+2 kv heads x head_dim 128, 9.8 GB at head_dim 256, bf16) at block ids near
+the end of the pool; the results must equal the oracle's on the small case
+(append bit-exact, attention to the bf16 tolerance)."""
 import numpy as np
 import pytest
 import torch
@@ -33,6 +33,36 @@ def _embed(case, dtype):
     kp[idx] = kp_small
     vp[idx] = vp_small
     return kp, vp, ids
+
+
+@pytest.mark.parametrize("cap", [0.0, 50.0])
+def test_prefill_head_dim_256_in_pools_over_4gib(cap):
+    """head_dim 256 through per-block descriptors (9.8 GB pools), with and
+    without softcap: ragged chunks over cached prefixes, a window, against the
+    oracle."""
+    case = wl.make_prefill_case(73, [100, 520, 0], [40, 77, 130], 8, 2, 256, "bf16", softcap=cap,
+                                window=300, q_scale=4.0)
+    print("\n[case] pools over 4 GiB: prefill at head_dim 256, softcap", cap, flush=True)
+    kp, vp, ids = _embed(case, "bf16")
+    assert (BIG_NB * 2 * 256 * 16 * 2) > (1 << 32)
+    bt = ids[case.block_tables]
+    slots = case.slot_mapping.astype(np.int64)
+    big_slots = np.where(slots >= 0, ids[np.maximum(slots, 0) // 16] * 16 + slots % 16, -1)
+    pkv.paged_kv_append(dev(case.k_new, "bf16"), dev(case.v_new, "bf16"), i32(big_slots), kp, vp)
+    q = dev(case.q, "bf16")
+    out = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:2], float("nan"), dtype=torch.float32, device="cuda")
+    pkv.paged_attn_prefill(out, q, i32(case.cu_q_lens), case.max_q_len, kp, vp, i32(bt),
+                           i32(case.context_lens), case.max_context_len, case.scale, case.softcap,
+                           case.window, lse=lse)
+    torch.cuda.synchronize()
+    kr, vr = oracle.append(case.k_new, case.v_new, case.slot_mapping, case.k_pool, case.v_pool, "bf16")
+    ref, ref_lse = oracle.prefill(case.q, case.cu_q_lens, kr, vr, case.block_tables,
+                                  case.context_lens, case.scale, case.softcap, case.window, "bf16")
+    check_close(as_f64(out), ref, "bf16", f"prefill D256 cap {cap}, pools over 4 GiB")
+    check_lse(lse.cpu().numpy().astype(np.float64), ref_lse, f"prefill D256 cap {cap}, pools over 4 GiB")
+    del kp, vp
+    torch.cuda.empty_cache()
 
 
 def test_prefill_append_and_decode_in_pools_over_4gib():
